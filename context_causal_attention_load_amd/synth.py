@@ -1,0 +1,115 @@
+"""Seeded synthetic inputs and workload shapes.
+
+This module only draws random numbers and names shapes; it holds none of the attention or
+load-balancing arithmetic, so both the HIP path's tests and the CPU oracle can take their
+inputs from it.
+
+Workload shapes stand in for the models the source pages test with: Llama2-7B (MHA, 32
+heads of 128) and Llama3.1-70B at 131072 tokens (64 query heads, 8 KV heads) from "Add
+context parallelism" (PR 1445, Tests); a DeepSeek-V3-style MLA attention (128 heads, q/k
+head dim 192 = 128 + 64 rotary, v head dim 128) from "Add support for EP to context
+parallelism in self-attention" (PR 2023, Tests); and a Mixtral-8x22B decode batch of 24 with
+prefill 1024 / target 2048 (48 query heads, 8 KV heads) from the inference benchmark command
+of "rename context to context_autoregressive" (issue 1453, Tests). Only the attention
+shapes are used; values are N(0, 1).
+
+Recipe: ``torch.Generator("cpu").manual_seed(seed)``; Q, then K, then V are drawn as
+float32 N(0,1) in natural token order, token chunk by token chunk (``TOKEN_CHUNK`` tokens
+per draw, all batches of a chunk at once), then rounded to the workload dtype with
+round-to-nearest-even (``Tensor.to``). Decode draws ``lengths`` (uniform integers in
+[len_min, len_max]) first, then q, then the K cache and the V cache over the full maximum
+length.
+"""
+
+from dataclasses import dataclass, field
+import math
+
+import torch
+
+TOKEN_CHUNK = 4096
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    batch: int
+    seq: int
+    cps: tuple
+    hq: int
+    hkv: int
+    d_qk: int
+    d_v: int
+    dtype: torch.dtype
+    seed: int
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.d_qk)
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    batch: int
+    hq: int
+    hkv: int
+    d: int
+    max_len: int
+    len_min: int
+    len_max: int
+    dtype: torch.dtype
+    seed: int
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.d)
+
+
+TINY_CP2_F32 = PrefillWorkload("tiny-cp2-gqa-fp32-s512", 1, 512, (2,), 4, 2, 64, 64, torch.float32, 1)
+LLAMA2_7B_S8K = PrefillWorkload("llama2-7b-mha-bf16-s8192", 1, 8192, (1, 4), 32, 32, 128, 128, torch.bfloat16, 2)
+LLAMA31_70B_S131K = PrefillWorkload("llama3.1-70b-gqa-bf16-s131072-cp8", 1, 131072, (8,), 64, 8, 128, 128, torch.bfloat16, 3)
+DEEPSEEK_V3_MLA_S32K = PrefillWorkload("deepseek-v3-mla-bf16-s32768-cp4", 1, 32768, (4,), 128, 128, 192, 128, torch.bfloat16, 4)
+MIXTRAL_8X22B_DECODE = DecodeWorkload("mixtral-8x22b-gqa-decode-b24-l2048", 24, 48, 8, 128, 2048, 1024, 2048, torch.bfloat16, 5)
+
+PREFILL_WORKLOADS = (TINY_CP2_F32, LLAMA2_7B_S8K, LLAMA31_70B_S131K, DEEPSEEK_V3_MLA_S32K)
+
+
+def _draw(gen, shape, dtype, token_axis=1):
+    """N(0,1) float32 draws, chunked along ``token_axis``, rounded to ``dtype``."""
+    n = shape[token_axis]
+    out = torch.empty(shape, dtype=dtype)
+    for t0 in range(0, n, TOKEN_CHUNK):
+        t1 = min(n, t0 + TOKEN_CHUNK)
+        sub = list(shape)
+        sub[token_axis] = t1 - t0
+        block = torch.randn(sub, generator=gen, dtype=torch.float32)
+        out.narrow(token_axis, t0, t1 - t0).copy_(block.to(dtype))
+    return out
+
+
+def prefill_inputs(batch, seq, hq, hkv, d_qk, d_v, dtype, seed):
+    """Q [B,S,Hq,Dqk], K [B,S,Hkv,Dqk], V [B,S,Hkv,Dv] in natural token order (CPU tensors)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    q = _draw(gen, (batch, seq, hq, d_qk), dtype)
+    k = _draw(gen, (batch, seq, hkv, d_qk), dtype)
+    v = _draw(gen, (batch, seq, hkv, d_v), dtype)
+    return q, k, v
+
+
+def workload_prefill_inputs(w: PrefillWorkload, seed=None):
+    return prefill_inputs(w.batch, w.seq, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype, w.seed if seed is None else seed)
+
+
+def decode_inputs(batch, hq, hkv, d, max_len, len_min, len_max, dtype, seed):
+    """lengths [B] int32, q [B,Hq,D], k_cache / v_cache [B,Hkv,Lmax,D] (CPU tensors)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    lengths = torch.randint(len_min, len_max + 1, (batch,), generator=gen, dtype=torch.int64).to(torch.int32)
+    q = torch.randn((batch, hq, d), generator=gen, dtype=torch.float32).to(dtype)
+    k_cache = _draw(gen, (batch, hkv, max_len, d), dtype, token_axis=2)
+    v_cache = _draw(gen, (batch, hkv, max_len, d), dtype, token_axis=2)
+    return lengths, q, k_cache, v_cache
+
+
+def workload_decode_inputs(w: DecodeWorkload, seed=None):
+    return decode_inputs(w.batch, w.hq, w.hkv, w.d, w.max_len, w.len_min, w.len_max, w.dtype,
+                         w.seed if seed is None else seed)

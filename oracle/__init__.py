@@ -1,0 +1,56 @@
+"""CPU fp64 oracle for load-balanced context-parallel causal attention and GQA decode.
+
+TEST INFRASTRUCTURE ONLY. This package is the slow, plainly written reference that the
+HIP path is checked against. Only the test suite, the smoke check in ``__graft_entry__``
+and the CPU-baseline leg of ``bench.py`` may import it. The product library never calls
+it, and it shares no code, tables or helpers with the HIP sources.
+
+Sources (web pages, cited by title and section):
+
+* "Add context parallelism" (MaxText PR 1445), Description: context parallelism
+  all-gathers keys/values and shards queries along the sequence; tokens *and the attention
+  mask* are reordered for load balance, with the cp=2 example giving one device tokens
+  0,1,6,7 and the other 2,3,4,5.
+* "Add support for EP to context parallelism in self-attention" (MaxText PR 2023),
+  Description / unit test: the sharded result is compared against un-sharded dot-product
+  attention (the role this oracle plays), with and without load balancing, for MHA and MLA.
+* "Add Pallas GPU decode attention in Maxtext inference" (MaxText PR 1066), Description /
+  Tests: grouped-query single-token decode attention over a KV cache filled to the current
+  length.
+
+Every function computes in float64 from inputs upcast exactly from their stored dtype.
+
+Parity status: every function here is pinned by ``tests/test_oracle.py`` (worked example
+printed on the pages, brute force, a library routine, closed forms and invariants). No
+function is "parity unpinned".
+"""
+
+from .lb_index import (
+    load_balance_perm,
+    inverse_perm,
+    shard_row_range,
+    shard_positions,
+    causal_pair_count,
+    contiguous_shard_positions,
+)
+from .attention import (
+    causal_attention_ref,
+    cp_attention_ref,
+    decode_ref,
+    permute_ref,
+    unpermute_ref,
+)
+
+__all__ = [
+    "load_balance_perm",
+    "inverse_perm",
+    "shard_row_range",
+    "shard_positions",
+    "causal_pair_count",
+    "contiguous_shard_positions",
+    "causal_attention_ref",
+    "cp_attention_ref",
+    "decode_ref",
+    "permute_ref",
+    "unpermute_ref",
+]

@@ -1,0 +1,367 @@
+"""Pins for the CPU oracle: worked example, brute force, library routines, closed forms.
+
+Every check here is independent of the oracle's own code path, so that a plausible mistake
+in the oracle (wrong chunk order, strict mask, dropped scale, wrong head group, transposed
+operand) fails at least one of them; ``test_planted_mistakes_are_caught`` plants such
+mistakes and confirms it.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as oatt
+from oracle import lb_index as olb
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def _rand(shape, seed, dtype=np.float64):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal(shape).astype(dtype)
+
+
+def _brute_force(q, k, v, q_pos, k_pos, scale):
+    """Pure-Python loops with math.fsum: the definition written element by element."""
+    B, Sq, Hq, Dqk = q.shape
+    Sk, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    G = Hq // Hkv
+    O = np.zeros((B, Sq, Hq, Dv))
+    L = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        for i in range(Sq):
+            for h in range(Hq):
+                g = h // G
+                s = {}
+                for j in range(Sk):
+                    if k_pos[j] <= q_pos[i]:
+                        s[j] = scale * math.fsum(float(q[b, i, h, d]) * float(k[b, j, g, d]) for d in range(Dqk))
+                m = max(s.values())
+                w = {j: math.exp(x - m) for j, x in s.items()}
+                l = math.fsum(w.values())
+                for d in range(Dv):
+                    O[b, i, h, d] = math.fsum(w[j] * float(v[b, j, g, d]) for j in w) / l
+                L[b, h, i] = m + math.log(l)
+    return O, L
+
+
+def _check_golden(perm_fn):
+    with open(os.path.join(GOLDEN, "lb_perm_s8_cp2.txt")) as f:
+        lines = [ln for ln in f if ln.strip() and not ln.startswith("#")]
+    assert lines
+    for ln in lines:
+        parts = [p.split() for p in ln.split("|")]
+        seq, cp = int(parts[0][0]), int(parts[0][1])
+        shards = [[int(x) for x in p] for p in parts[1:]]
+        perm = list(perm_fn(seq, cp))
+        n = seq // cp
+        got = [perm[r * n:(r + 1) * n] for r in range(cp)]
+        assert got == shards, (got, shards)
+
+
+def _check_balance(perm_fn, seq, cp):
+    perm = np.asarray(perm_fn(seq, cp))
+    assert sorted(perm.tolist()) == list(range(seq))
+    n = seq // cp
+    counts = [olb.causal_pair_count(perm[r * n:(r + 1) * n], perm) for r in range(cp)]
+    # closed form: every rank holds chunk r and chunk 2cp-1-r, c*(S+1) visible pairs
+    assert counts == [seq * (seq + 1) // (2 * cp)] * cp, counts
+
+
+def _check_brute(att_fn, seq, cp, hq, hkv, dqk, dv, seed):
+    q = _rand((1, seq, hq, dqk), seed)
+    k = _rand((1, seq, hkv, dqk), seed + 1)
+    v = _rand((1, seq, hkv, dv), seed + 2)
+    scale = 1.0 / math.sqrt(dqk)
+    perm = olb.load_balance_perm(seq, cp)
+    qp, kp, vp = q[:, perm], k[:, perm], v[:, perm]
+    for r in range(cp):
+        b0, b1 = olb.shard_row_range(seq, cp, r)
+        pos = perm[b0:b1]
+        O, L = att_fn(qp[:, b0:b1], kp, vp, pos, perm, scale)
+        Ob, Lb = _brute_force(qp[:, b0:b1], kp, vp, pos, perm, scale)
+        np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L, Lb, rtol=0, atol=1e-12)
+
+
+def _sdpa_full(q, k, v, scale):
+    """torch's CPU fp64 scaled_dot_product_attention (causal) plus torch.logsumexp: library pins."""
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)  # B H S D
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3)
+    G = tq.shape[1] // tk.shape[1]
+    tk = tk.repeat_interleave(G, dim=1)
+    tv = tv.repeat_interleave(G, dim=1)
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale)
+    s = torch.matmul(tq, tk.transpose(-1, -2).contiguous()) * scale
+    S = s.shape[-1]
+    causal = torch.ones(S, S, dtype=torch.bool).tril()
+    lse = torch.logsumexp(s.masked_fill(~causal, float("-inf")), dim=-1)
+    return out.permute(0, 2, 1, 3).numpy(), lse.numpy()
+
+
+def _check_library(att_fn, seq, cp, hq, hkv, dqk, dv, seed, batch=1):
+    q = _rand((batch, seq, hq, dqk), seed)
+    k = _rand((batch, seq, hkv, dqk), seed + 1)
+    v = _rand((batch, seq, hkv, dv), seed + 2)
+    scale = 1.0 / math.sqrt(dqk)
+    perm = olb.load_balance_perm(seq, cp)
+    inv = olb.inverse_perm(perm)
+    qp, kp, vp = q[:, perm], k[:, perm], v[:, perm]
+    Os, Ls = [], []
+    for r in range(cp):
+        b0, b1 = olb.shard_row_range(seq, cp, r)
+        O, L = att_fn(qp[:, b0:b1], kp, vp, perm[b0:b1], perm, scale)
+        Os.append(O)
+        Ls.append(L)
+    O_perm = np.concatenate(Os, axis=1)
+    L_perm = np.concatenate(Ls, axis=2)
+    O_nat = O_perm[:, inv]
+    L_nat = L_perm[:, :, inv]
+    O_ref, L_ref = _sdpa_full(q, k, v, scale)
+    np.testing.assert_allclose(O_nat, O_ref, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(L_nat, L_ref, rtol=0, atol=1e-10)
+
+
+def _oracle_att(q, k, v, q_pos, k_pos, scale):
+    return oatt.causal_attention_ref(q, k, v, q_pos, k_pos, scale)
+
+
+# ----------------------------------------------------------------------------- index pins
+
+def test_golden_worked_example():
+    _check_golden(olb.load_balance_perm)
+
+
+@pytest.mark.parametrize("seq,cp", [(8, 1), (8, 2), (8, 4), (512, 2), (8192, 4), (131072, 8), (32768, 4), (96, 3)])
+def test_balance_closed_form(seq, cp):
+    _check_balance(olb.load_balance_perm, seq, cp)
+
+
+def test_contiguous_sharding_is_unbalanced():
+    # max/mean visible-pair ratio of contiguous shards: 1.5 (S=512,cp=2), 1.875 (S=131072,cp=8)
+    for seq, cp, ratio in [(512, 2, 1.5), (8192, 4, 1.75), (131072, 8, 1.875), (32768, 4, 1.75)]:
+        allpos = np.arange(seq)
+        counts = [olb.causal_pair_count(olb.contiguous_shard_positions(seq, cp, r), allpos) for r in range(cp)]
+        mean = seq * (seq + 1) / (2 * cp)
+        assert abs(max(counts) / mean - ratio) < 2e-3, (seq, cp, max(counts) / mean)
+
+
+@pytest.mark.parametrize("seq,cp", [(8, 2), (64, 4), (48, 3), (512, 2), (4096, 8)])
+def test_permutation_round_trip_bit_exact(seq, cp):
+    perm = olb.load_balance_perm(seq, cp)
+    inv = olb.inverse_perm(perm)
+    assert (perm[inv] == np.arange(seq)).all() and (inv[perm] == np.arange(seq)).all()
+    x = torch.randint(-2**31, 2**31 - 1, (2, seq, 3), dtype=torch.int32)
+    y = torch.cat([oatt.permute_ref(x, seq, cp, b0, b1 - b0)
+                   for b0, b1 in (olb.shard_row_range(seq, cp, r) for r in range(cp))], dim=1)
+    assert torch.equal(y, oatt.permute_ref(x, seq, cp))
+    z = torch.zeros_like(x)
+    for r in range(cp):
+        b0, b1 = olb.shard_row_range(seq, cp, r)
+        z = oatt.unpermute_ref(y[:, b0:b1], z, seq, cp, b0)
+    assert torch.equal(z, x)
+
+
+def test_index_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        olb.load_balance_perm(10, 2)
+    with pytest.raises(ValueError):
+        olb.shard_row_range(16, 2, 2)
+
+
+# ----------------------------------------------------------------------------- attention pins
+
+@pytest.mark.parametrize("seq,cp,hq,hkv,dqk,dv", [
+    (8, 1, 2, 2, 4, 4), (8, 2, 4, 2, 4, 4), (16, 4, 2, 1, 3, 5), (16, 2, 4, 4, 6, 4), (12, 3, 2, 2, 4, 4)])
+def test_brute_force(seq, cp, hq, hkv, dqk, dv):
+    _check_brute(_oracle_att, seq, cp, hq, hkv, dqk, dv, seed=seq * 7 + cp)
+
+
+@pytest.mark.parametrize("seq,cp,hq,hkv,dqk,dv,batch", [
+    (64, 1, 4, 2, 16, 16, 1), (64, 2, 4, 2, 16, 16, 2), (128, 4, 6, 2, 12, 8, 1),
+    (256, 8, 8, 8, 16, 16, 1), (96, 3, 4, 1, 8, 8, 1)])
+def test_sharded_equals_library_causal_attention(seq, cp, hq, hkv, dqk, dv, batch):
+    _check_library(_oracle_att, seq, cp, hq, hkv, dqk, dv, seed=seq + cp, batch=batch)
+
+
+def test_cp_degrees_agree():
+    seq, hq, hkv, d = 128, 4, 2, 16
+    q, k, v = _rand((1, seq, hq, d), 1), _rand((1, seq, hkv, d), 2), _rand((1, seq, hkv, d), 3)
+    outs = {}
+    for cp in (1, 2, 4, 8):
+        perm = olb.load_balance_perm(seq, cp)
+        inv = olb.inverse_perm(perm)
+        Os, Ls = [], []
+        for r in range(cp):
+            b0, b1 = olb.shard_row_range(seq, cp, r)
+            O, L = oatt.cp_attention_ref(q[:, perm][:, b0:b1], k[:, perm], v[:, perm], perm[b0:b1], seq, cp, 0.25)
+            Os.append(O)
+            Ls.append(L)
+        outs[cp] = (np.concatenate(Os, 1)[:, inv], np.concatenate(Ls, 2)[:, :, inv])
+    for cp in (2, 4, 8):
+        np.testing.assert_allclose(outs[cp][0], outs[1][0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(outs[cp][1], outs[1][1], rtol=0, atol=1e-12)
+
+
+def test_constant_v_returns_v():
+    seq, cp = 64, 4
+    perm = olb.load_balance_perm(seq, cp)
+    q, k = _rand((1, seq, 4, 8), 5), _rand((1, seq, 2, 8), 6)
+    vrow = _rand((2, 8), 7)
+    v = np.broadcast_to(vrow, (1, seq, 2, 8)).copy()
+    for r in range(cp):
+        b0, b1 = olb.shard_row_range(seq, cp, r)
+        O, _ = oatt.cp_attention_ref(q[:, perm][:, b0:b1], k[:, perm], v[:, perm], perm[b0:b1], seq, cp, 0.3)
+        for h in range(4):
+            np.testing.assert_allclose(O[0, :, h, :], np.broadcast_to(vrow[h // 2], (b1 - b0, 8)), rtol=0, atol=1e-12)
+
+
+def test_identical_keys_give_prefix_mean():
+    seq, cp, scale = 64, 2, 0.7
+    perm = olb.load_balance_perm(seq, cp)
+    q, v = _rand((1, seq, 2, 8), 8), _rand((1, seq, 1, 8), 9)
+    krow = _rand((8,), 10)
+    k = np.broadcast_to(krow, (1, seq, 1, 8)).copy()
+    prefix_mean = np.cumsum(v[0, :, 0, :], axis=0) / np.arange(1, seq + 1)[:, None]
+    for r in range(cp):
+        b0, b1 = olb.shard_row_range(seq, cp, r)
+        pos = perm[b0:b1]
+        O, L = oatt.cp_attention_ref(q[:, perm][:, b0:b1], k[:, perm], v[:, perm], pos, seq, cp, scale)
+        for h in range(2):
+            np.testing.assert_allclose(O[0, :, h, :], prefix_mean[pos], rtol=0, atol=1e-12)
+            expect = scale * (q[0, pos, h, :] @ krow) + np.log(pos + 1.0)
+            np.testing.assert_allclose(L[0, h], expect, rtol=0, atol=1e-12)
+
+
+def test_position_zero_row_and_lse_bounds():
+    seq, cp, scale = 32, 2, 0.5
+    perm = olb.load_balance_perm(seq, cp)
+    q, k, v = _rand((1, seq, 2, 4), 11), _rand((1, seq, 2, 4), 12), _rand((1, seq, 2, 4), 13)
+    b0, b1 = olb.shard_row_range(seq, cp, 0)
+    pos = perm[b0:b1]
+    O, L = oatt.cp_attention_ref(q[:, perm][:, b0:b1], k[:, perm], v[:, perm], pos, seq, cp, scale)
+    i0 = int(np.nonzero(pos == 0)[0][0])
+    for h in range(2):
+        assert np.array_equal(O[0, i0, h], v[0, 0, h])
+        assert L[0, h, i0] == scale * float(q[0, 0, h] @ k[0, 0, h])
+    # max_j s_j <= LSE_i <= max_j s_j + ln(n_i)
+    for i, p in enumerate(pos):
+        for h in range(2):
+            s = scale * (k[0, :p + 1, h] @ q[0, p, h])
+            assert s.max() - 1e-12 <= L[0, h, i] <= s.max() + math.log(p + 1) + 1e-12
+
+
+def test_rows_subset_matches_full():
+    seq, cp = 128, 4
+    perm = olb.load_balance_perm(seq, cp)
+    q, k, v = _rand((1, seq, 4, 8), 14), _rand((1, seq, 2, 8), 15), _rand((1, seq, 2, 8), 16)
+    b0, b1 = olb.shard_row_range(seq, cp, 1)
+    full = oatt.cp_attention_ref(q[:, perm][:, b0:b1], k[:, perm], v[:, perm], perm[b0:b1], seq, cp, 0.3)
+    rows = [0, 5, 15, 16, 30, 31]
+    part = oatt.cp_attention_ref(q[:, perm][:, b0:b1], k[:, perm], v[:, perm], perm[b0:b1], seq, cp, 0.3, rows=rows)
+    np.testing.assert_array_equal(part[0][:, rows], full[0][:, rows])
+    np.testing.assert_array_equal(part[1][:, :, rows], full[1][:, :, rows])
+
+
+# ----------------------------------------------------------------------------- decode pins
+
+def _check_decode(dec_fn):
+    B, Hq, Hkv, D, Lmax = 3, 6, 2, 8, 40
+    rng = np.random.default_rng(21)
+    lengths = np.array([1, 17, 40])
+    q = rng.standard_normal((B, Hq, D))
+    kc = rng.standard_normal((B, Hkv, Lmax, D))
+    vc = rng.standard_normal((B, Hkv, Lmax, D))
+    scale = 0.35
+    O, L = dec_fn(q, kc, vc, lengths, scale)
+    for b in range(B):
+        n = lengths[b]
+        # the newest token sits at cache index n-1 and sees keys 0..n-1: last row of causal attention
+        qq = q[b][None, None]  # [1, 1, Hq, D]
+        kk = kc[b, :, :n].transpose(1, 0, 2)[None]
+        vv = vc[b, :, :n].transpose(1, 0, 2)[None]
+        Oc, Lc = _brute_force(qq, kk, vv, [n - 1], list(range(n)), scale)
+        np.testing.assert_allclose(O[b], Oc[0, 0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L[b], Lc[0, :, 0], rtol=0, atol=1e-12)
+        # library routine: non-causal SDPA over the valid prefix
+        tq = torch.from_numpy(q[b][:, None, :])  # Hq 1 D
+        tk = torch.from_numpy(kc[b, :, :n]).repeat_interleave(Hq // Hkv, 0)
+        tv = torch.from_numpy(vc[b, :, :n]).repeat_interleave(Hq // Hkv, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)
+        np.testing.assert_allclose(O[b], ref[:, 0].numpy(), rtol=0, atol=1e-12)
+    # NaN-poisoned tail must not change anything
+    kc2, vc2 = kc.copy(), vc.copy()
+    for b in range(B):
+        kc2[b, :, lengths[b]:] = np.nan
+        vc2[b, :, lengths[b]:] = np.nan
+    O2, L2 = dec_fn(q, kc2, vc2, lengths, scale)
+    assert np.array_equal(O2, O) and np.array_equal(L2, L)
+
+
+def test_decode_pins():
+    _check_decode(oatt.decode_ref)
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+
+def _perm_swapped_chunk_order(seq, cp):
+    c = seq // (2 * cp)
+    out = []
+    for r in range(cp):
+        out += list(range((2 * cp - 1 - r) * c, (2 * cp - r) * c)) + list(range(r * c, (r + 1) * c))
+    return np.array(out)
+
+
+def _perm_unbalanced(seq, cp):
+    c = seq // (2 * cp)
+    out = []
+    for r in range(cp):
+        out += list(range(r * c, (r + 1) * c)) + list(range((cp + r) * c, (cp + r + 1) * c))
+    return np.array(out)
+
+
+def _att_strict_mask(q, k, v, q_pos, k_pos, scale):
+    return oatt.causal_attention_ref(q, k, v, np.asarray(q_pos) - 1, k_pos, scale)
+
+
+def _att_no_scale(q, k, v, q_pos, k_pos, scale):
+    return oatt.causal_attention_ref(q, k, v, q_pos, k_pos, 1.0)
+
+
+def _att_wrong_group(q, k, v, q_pos, k_pos, scale):
+    # query head h reads kv head h % Hkv instead of h // G
+    Hq, Hkv = q.shape[2], k.shape[2]
+    idx = [h % Hkv for h in range(Hq)]
+    kk = np.asarray(k)[:, :, idx]
+    vv = np.asarray(v)[:, :, idx]
+    return oatt.causal_attention_ref(q, kk, vv, q_pos, k_pos, scale)
+
+
+def _att_transposed_v(q, k, v, q_pos, k_pos, scale):
+    vv = np.asarray(v)[:, ::-1]  # values taken from the mirrored token
+    return oatt.causal_attention_ref(q, k, vv, q_pos, k_pos, scale)
+
+
+def _dec_off_by_one(q, kc, vc, lengths, scale):
+    return oatt.decode_ref(q, kc, vc, np.asarray(lengths) - 1 + (np.asarray(lengths) == 1), scale)
+
+
+@pytest.mark.parametrize("check", [
+    lambda: _check_golden(_perm_swapped_chunk_order),
+    lambda: _check_balance(_perm_unbalanced, 64, 4),
+    lambda: _check_brute(_att_strict_mask, 8, 2, 2, 2, 4, 4, 3),
+    lambda: _check_library(_att_no_scale, 64, 2, 4, 2, 16, 16, 3),
+    lambda: _check_library(_att_wrong_group, 64, 2, 4, 2, 16, 16, 3),
+    lambda: _check_brute(_att_transposed_v, 8, 2, 2, 1, 4, 4, 3),
+    lambda: _check_decode(_dec_off_by_one),
+], ids=["chunk-order", "unbalanced", "strict-mask", "no-scale", "wrong-group", "mirrored-v", "decode-length"])
+def test_planted_mistakes_are_caught(check):
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        check()

@@ -1,0 +1,225 @@
+"""Benchmark: one context-parallel rank's load-balanced causal GQA attention step on one MI355X.
+
+Workload (default): Llama3.1-70B-shaped attention at 131072 tokens, 64 query heads / 8 KV
+heads, head dim 128, bf16, cp = 8 (one rank's 16384-row query shard over the full K/V). One
+step = the rank's whole share of the hot path, inputs resident in HBM:
+  1. gather its query shard (window r*2c .. (r+1)*2c of the load-balanced order) from Q,
+  2. gather its K and V shard into its slice of the all-gathered K/V buffers (the other ranks'
+     slices were filled before timing: the all-gather itself needs other GPUs),
+  3. causal attention forward over the full K/V (O and LSE),
+  4. scatter O and LSE back to original token order.
+Step i runs rank i % cp, so the timed steps cover every rank; per-rank times are reported.
+
+Also measured: GQA decode (Mixtral-8x22B shape, batch 24, 48/8 heads, D 128, cache 2048 with
+lengths uniform in [1024, 2048]), rotating 4 cache copies so reads come from HBM rather than
+the 256 MB last-level cache; and the CPU fp64 oracle on a bounded row sample of the same
+prefill workload (the CPU baseline).
+
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+METRIC = "causal attn fwd TFLOP/s + %MFMA peak (131k CP shard); decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def useful_flops(seq, cp, hq, dqk, dv, batch=1):
+    # every rank of a balanced split sees exactly c*(S+1) causal (query, key) pairs
+    c = seq // (2 * cp)
+    pairs = c * (seq + 1)
+    return 2.0 * pairs * hq * (dqk + dv) * batch
+
+
+def bench_prefill(w, cp, steps, warmup, dev):
+    import context_causal_attention_load_amd as cpa
+    from context_causal_attention_load_amd import synth
+
+    q, k, v = synth.workload_prefill_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    del q, k, v
+    S, c = w.seq, w.seq // (2 * cp)
+    kp, vp = cpa.permute(kd, cp), cpa.permute(vd, cp)  # the all-gathered K/V (all ranks' slices)
+    q_shard = torch.empty((w.batch, 2 * c, w.hq, w.d_qk), dtype=w.dtype, device=dev)
+    o_shard = torch.empty((w.batch, 2 * c, w.hq, w.d_v), dtype=w.dtype, device=dev)
+    lse_shard = torch.empty((w.batch, w.hq, 2 * c), dtype=torch.float32, device=dev)
+    o_nat = torch.zeros((w.batch, S, w.hq, w.d_v), dtype=w.dtype, device=dev)
+    lse_nat = torch.zeros((w.batch, w.hq, S), dtype=torch.float32, device=dev)
+    assert w.batch == 1, "the K/V slice update below assumes batch 1"
+
+    def step(r, ev=None):
+        b0 = r * 2 * c
+        cpa.permute(qd, cp, row_begin=b0, row_count=2 * c, out=q_shard)
+        cpa.permute(kd, cp, row_begin=b0, row_count=2 * c, out=kp[:, b0:b0 + 2 * c])
+        cpa.permute(vd, cp, row_begin=b0, row_count=2 * c, out=vp[:, b0:b0 + 2 * c])
+        if ev is not None:
+            ev[0].record()
+        cpa.attention_fwd(q_shard, kp, vp, cp, r, scale=w.scale, out=o_shard, lse=lse_shard)
+        if ev is not None:
+            ev[1].record()
+        cpa.unpermute(o_shard, cp, S, row_begin=b0, out=o_nat)
+        cpa.unpermute(lse_shard, cp, S, dim=2, row_begin=b0, out=lse_nat)
+
+    for i in range(warmup):
+        step(i % cp)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step_evs[i][0].record()
+        step(i % cp, evs[i])
+        step_evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    step_ms = [a.elapsed_time(b) for a, b in step_evs]
+    per_rank = {}
+    for i in range(steps):
+        per_rank.setdefault(i % cp, []).append(step_ms[i])
+    return dict(wall_s=wall, attn_ms=attn_ms, step_ms=step_ms,
+                per_rank_ms={r: sum(v) / len(v) for r, v in sorted(per_rank.items())},
+                flops=useful_flops(S, cp, w.hq, w.d_qk, w.d_v, w.batch))
+
+
+def bench_decode(w, iters, dev, copies=4):
+    import context_causal_attention_load_amd as cpa
+    from context_causal_attention_load_amd import synth
+
+    lengths, q, kc, vc = synth.workload_decode_inputs(w)
+    qd, ld = q.to(dev), lengths.to(dev)
+    caches = [(kc.to(dev), vc.to(dev))]
+    for _ in range(copies - 1):
+        caches.append((caches[0][0].clone(), caches[0][1].clone()))
+    ws = torch.empty(cpa.decode_workspace_bytes(w.batch, w.hq, w.hkv, w.max_len, w.d), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.batch, w.hq, w.d), dtype=w.dtype, device=dev)
+    lse = torch.empty((w.batch, w.hq), dtype=torch.float32, device=dev)
+    for i in range(copies):
+        cpa.decode(qd, caches[i][0], caches[i][1], ld, scale=w.scale, workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        kci, vci = caches[i % copies]
+        evs[i][0].record()
+        cpa.decode(qd, kci, vci, ld, scale=w.scale, workspace=ws, out=out, lse=lse)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    elt = 2
+    kv_bytes = int(lengths.sum()) * w.hkv * w.d * elt * 2
+    io_bytes = w.batch * w.hq * w.d * elt * 2 + w.batch * w.hq * 4 + w.batch * 4
+    alg = kv_bytes + io_bytes
+    med = ms[len(ms) // 2]
+    return dict(median_ms=med, min_ms=ms[0], bytes=alg, gbs=alg / (med * 1e-3) / 1e9)
+
+
+def cpu_baseline(w, cp, rank, n_rows, seed=0):
+    """Time the CPU fp64 oracle (as it is) on a row sample of one rank: its permutes of the
+    rank's windows plus attention for ``n_rows`` query rows over all heads."""
+    import numpy as np
+
+    from context_causal_attention_load_amd import synth
+    from oracle import attention as oatt
+    from oracle import lb_index as olb
+
+    q, k, v = synth.workload_prefill_inputs(w)
+    S, c = w.seq, w.seq // (2 * cp)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(rng.integers(0, 2 * c, n_rows))
+    pos = olb.shard_positions(S, cp, rank)
+    t0 = time.perf_counter()
+    qs = oatt.permute_ref(q, S, cp, rank * 2 * c, 2 * c)[:, rows]
+    kp = oatt.permute_ref(k, S, cp)
+    vp = oatt.permute_ref(v, S, cp)
+    oatt.cp_attention_ref(qs, kp, vp, pos[rows], S, cp, w.scale)
+    dt = time.perf_counter() - t0
+    pairs = int((pos[rows] + 1).sum())
+    flops = 2.0 * pairs * w.hq * (w.d_qk + w.d_v) * w.batch
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=torch.get_num_threads(), kind="oracle",
+                sample=(f"{len(rows)} random query rows (all {w.hq} heads) of rank {rank} at S={S}, cp={cp}: "
+                        f"oracle permutes of Q window and full K/V plus fp64 attention, {dt:.1f} s, "
+                        f"{flops / 1e12:.3f} useful TFLOP"),
+                seconds=dt)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=16)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-iters", type=int, default=50)
+    ap.add_argument("--cpu-rows", type=int, default=24)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share (one context-parallel rank); runs on more than one GPU "
+              "are not part of this build", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    from context_causal_attention_load_amd import synth
+
+    dev = "cuda:0"
+    w = synth.LLAMA31_70B_S131K
+    cp = w.cps[0]
+    pre = bench_prefill(w, cp, args.steps, args.warmup, dev)
+    ms_per_step = sum(pre["step_ms"]) / len(pre["step_ms"])
+    value = pre["flops"] / (ms_per_step * 1e-3) / 1e12
+    attn_avg_ms = sum(pre["attn_ms"]) / len(pre["attn_ms"])
+    achieved = pre["flops"] / (attn_avg_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: one rank's 16384-row query shard over full K/V", "batch": w.batch,
+                   "seq_len": w.seq, "cp": cp, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim_qk": w.d_qk,
+                   "head_dim_v": w.d_v, "parallelism": "one context-parallel rank (cp=8) per GPU",
+                   "ranks_timed": sorted(pre["per_rank_ms"].keys())},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd_bf16_kernel<128,128>", "kernel_avg_ms": round(attn_avg_ms, 4),
+                     "useful_flop_per_launch": pre["flops"]},
+        "per_rank_step_ms": {str(r): round(t, 3) for r, t in pre["per_rank_ms"].items()},
+    }
+    if not args.no_decode:
+        dw = synth.MIXTRAL_8X22B_DECODE
+        d = bench_decode(dw, args.decode_iters, dev)
+        result["decode"] = {"workload": dw.name, "value": round(d["gbs"], 1), "unit": "GB/s",
+                            "median_us": round(d["median_ms"] * 1e3, 2), "min_us": round(d["min_ms"] * 1e3, 2),
+                            "roofline": {"bound": "hbm", "achieved": round(d["gbs"], 1), "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": round(d["gbs"] / PEAK_HBM_GBS, 4),
+                                         "traffic": None, "algorithmic_bytes": d["bytes"]}}
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, cp, 0, args.cpu_rows)
+        cb.pop("seconds")
+        result["cpu_baseline"] = {k: (round(v, 5) if isinstance(v, float) else v) for k, v in cb.items()}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

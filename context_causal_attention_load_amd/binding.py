@@ -1,0 +1,217 @@
+"""ctypes binding of libcpattn.so (include/cpattn.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype and contiguity and
+passed as raw pointers with the current HIP stream. Every computation runs in the library's
+HIP kernels; there is no CPU path. A missing library raises ``CpattnError`` on first use.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+from .build import OUT as _LIB_PATH
+
+CPA_OK, CPA_EINVAL, CPA_ENOTSUP, CPA_EHIP = 0, -22, -95, -1000
+CPA_F32, CPA_BF16 = 0, 1
+
+_DTYPES = {torch.float32: CPA_F32, torch.bfloat16: CPA_BF16}
+
+_lib = None
+
+
+class CpattnError(RuntimeError):
+    def __init__(self, func, status, message):
+        super().__init__(f"{func} failed with status {status}: {message}")
+        self.status = status
+        self.func = func
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libcpattn.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise CpattnError("load_library", CPA_EHIP,
+                          f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(python -m context_causal_attention_load_amd.build)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    lib.cpattn_last_error.restype = ctypes.c_char_p
+    lib.cpattn_last_error.argtypes = []
+    lib.cp_load_balance_source_index.restype = i64
+    lib.cp_load_balance_source_index.argtypes = [i64, i32, i64]
+    lib.cp_load_balance_positions.restype = ctypes.c_int
+    lib.cp_load_balance_positions.argtypes = [i64, i32, i64, i64, vp]
+    for name in ("cp_load_balance_permute", "cp_load_balance_unpermute"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, i64, i64, i64, i32, i64, i64, vp]
+    lib.cp_attention_fwd.restype = ctypes.c_int
+    lib.cp_attention_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                     f32, i32, i32, vp]
+    lib.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.gqa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.gqa_decode_attention.restype = ctypes.c_int
+    lib.gqa_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                         vp, ctypes.c_size_t, vp]
+    _lib = lib
+    return lib
+
+
+def _check(name, status):
+    if status != CPA_OK:
+        msg = load_library().cpattn_last_error().decode(errors="replace")
+        raise CpattnError(name, status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_gpu(*tensors):
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous (no implicit copies are made)")
+
+
+# ---------------------------------------------------------------------------- index helpers
+
+def lb_source_index(seq, cp, j):
+    """Original position of permuted slot j (host helper of the library)."""
+    return int(load_library().cp_load_balance_source_index(seq, cp, j))
+
+
+def lb_positions(seq, cp, row_begin=0, row_count=None):
+    """int32 CPU tensor of original positions for permuted slots [row_begin, row_begin+row_count)."""
+    if row_count is None:
+        row_count = seq - row_begin
+    out = torch.empty(row_count, dtype=torch.int32)
+    _check("cp_load_balance_positions",
+           load_library().cp_load_balance_positions(seq, cp, row_begin, row_count,
+                                                    ctypes.c_void_p(out.data_ptr())))
+    return out
+
+
+# ---------------------------------------------------------------------------- permutation
+
+def _fold(x, dim):
+    dim = dim % x.dim()
+    outer = math.prod(x.shape[:dim])
+    row_bytes = math.prod(x.shape[dim + 1:]) * x.element_size()
+    return outer, x.shape[dim], row_bytes
+
+
+def permute(x, cp, dim=1, row_begin=0, row_count=None, out=None):
+    """Gather permuted slots [row_begin, row_begin+row_count) of ``x`` (original order along
+    ``dim``): ``out.select(dim, i) = x.select(dim, src(row_begin + i))``."""
+    _need_gpu(x, out)
+    outer, seq, row_bytes = _fold(x, dim)
+    if row_count is None:
+        row_count = seq - row_begin
+    shape = list(x.shape)
+    shape[dim % x.dim()] = row_count
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif list(out.shape) != shape or out.dtype != x.dtype:
+        raise ValueError(f"out must be {shape} {x.dtype}")
+    _check("cp_load_balance_permute",
+           load_library().cp_load_balance_permute(_ptr(x), _ptr(out), outer, seq, row_bytes, cp,
+                                                  row_begin, row_count, _stream(x.device)))
+    return out
+
+
+def unpermute(x, cp, seq, dim=1, row_begin=0, out=None):
+    """Scatter permuted slots [row_begin, row_begin + x.shape[dim]) back to original order:
+    ``out.select(dim, src(row_begin + i)) = x.select(dim, i)``. Other rows of ``out`` keep their
+    contents (a new ``out`` is zero-filled)."""
+    _need_gpu(x, out)
+    outer, row_count, row_bytes = _fold(x, dim)
+    shape = list(x.shape)
+    shape[dim % x.dim()] = seq
+    if out is None:
+        out = torch.zeros(shape, dtype=x.dtype, device=x.device)
+    elif list(out.shape) != shape or out.dtype != x.dtype:
+        raise ValueError(f"out must be {shape} {x.dtype}")
+    _check("cp_load_balance_unpermute",
+           load_library().cp_load_balance_unpermute(_ptr(x), _ptr(out), outer, seq, row_bytes, cp,
+                                                    row_begin, row_count, _stream(x.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------- attention
+
+def attention_fwd(q_shard, k, v, cp, rank, q_positions=None, scale=None, out=None, lse=None,
+                  want_lse=True):
+    """One rank's causal GQA attention over all-gathered K/V in load-balanced order.
+
+    q_shard [B, Sq, Hq, Dqk]; k [B, S, Hkv, Dqk]; v [B, S, Hkv, Dv]; q_positions int32 [Sq] on
+    the GPU or None (the rank's own shard). Returns (O [B, Sq, Hq, Dv], LSE [B, Hq, Sq] fp32).
+    """
+    _need_gpu(q_shard, k, v, q_positions, out, lse)
+    if q_shard.dtype not in _DTYPES or k.dtype != q_shard.dtype or v.dtype != q_shard.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, Sq, Hq, Dqk = q_shard.shape
+    S, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if k.shape != (B, S, Hkv, Dqk) or v.shape[:3] != (B, S, Hkv):
+        raise ValueError("k/v shapes do not match q")
+    if q_positions is not None and (q_positions.dtype != torch.int32 or q_positions.shape != (Sq,)):
+        raise ValueError("q_positions must be int32 [Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, Dv), dtype=q_shard.dtype, device=q_shard.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q_shard.device)
+    _check("cp_attention_fwd",
+           load_library().cp_attention_fwd(_ptr(q_shard), _ptr(k), _ptr(v), _ptr(q_positions), _ptr(out),
+                                           _ptr(lse), B, S, Sq, Hq, Hkv, Dqk, Dv, _DTYPES[q_shard.dtype],
+                                           float(scale), cp, rank, _stream(q_shard.device)))
+    return out, lse
+
+
+def decode_workspace_bytes(batch, hq, hkv, max_len, d):
+    return int(load_library().gqa_decode_workspace_bytes(batch, hq, hkv, max_len, d))
+
+
+def decode(q, k_cache, v_cache, lengths, scale=None, workspace=None, out=None, lse=None, want_lse=True):
+    """GQA single-token decode. q [B, Hq, D]; caches [B, Hkv, Lmax, D]; lengths int32 [B] (GPU).
+    Returns (O [B, Hq, D], LSE [B, Hq] fp32)."""
+    _need_gpu(q, k_cache, v_cache, lengths, workspace, out, lse)
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and caches must share dtype float32 or bfloat16")
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, Hkv, Lmax, D) or v_cache.shape != (B, Hkv, Lmax, D):
+        raise ValueError("cache shapes do not match q")
+    if lengths.dtype != torch.int32 or lengths.shape != (B,):
+        raise ValueError("lengths must be int32 [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_workspace_bytes(B, Hq, Hkv, Lmax, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check("gqa_decode_attention",
+           load_library().gqa_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lengths), _ptr(out),
+                                               _ptr(lse), B, Hq, Hkv, D, Lmax, _DTYPES[q.dtype], float(scale),
+                                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                               _stream(q.device)))
+    return out, lse

@@ -1,0 +1,674 @@
+// Causal grouped-query attention forward over one context-parallel rank's query shard, for
+// gfx950 (MI355X).
+//
+// What it computes ("Add context parallelism", PR 1445, Description; "Add support for EP to
+// context parallelism in self-attention", PR 2023, unit test): for each query row i of the
+// shard and query head h, softmax(scale * q_i . k_j) v_j over the keys j whose original
+// position src(j) is <= the row's original position, with K/V given in the all-gathered
+// (load-balanced) order; plus the row log-sum-exp.
+//
+// Design (bf16):
+//  * A workgroup is 8 wavefronts. It owns `hpw` query heads of one KV group and 32*8/hpw query
+//    rows; each wave owns one head and 32 rows. All waves stream the same K/V tiles (64 keys)
+//    through LDS, so one tile serves every head of the group that the workgroup holds.
+//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K (row-major
+//    in LDS) is the A operand, the Q fragment lives in registers as the B operand. In the
+//    result each lane holds 16 keys of ONE query row, so row max/sum need a single exchange
+//    with the lane 32 away (v_permlane32_swap), and the probabilities already sit in the B
+//    operand layout of the next product O^T += V^T P^T. V^T comes straight from the row-major
+//    V tile with the gfx950 transposing LDS read (ds_read_b64_tr_b16).
+//  * Online softmax in fp32 with base-2 exponentials; the running max is only raised when a
+//    tile's max exceeds it by more than 8 (log2 units), so most tiles skip the O rescale.
+//  * Probabilities are rounded to bf16 once; the row sum adds those rounded values
+//    (v_dot2 with ones), so O is an exact convex combination of the bf16 weights.
+//  * Causal structure of a balanced shard: KV tiles are visited chunk by chunk in original
+//    order, chunk i sitting at permuted offset lb_chunk_offset(i). Only keys with position
+//    <= the workgroup's largest query position are visited; tiles whose last key position is
+//    <= its smallest query position skip the mask.
+//  * Global->LDS staging is double-buffered through registers: the loads for tile t+1 are in
+//    flight while tile t is computed. LDS rows use an XOR swizzle of 16-byte chunks.
+//  * Workgroup order is XCD-aware and heavy-first: consecutive work items (same KV head,
+//    neighbouring row blocks) go to the same XCD so they share its L2, and row blocks with the
+//    latest positions (most keys) start first.
+#include "common.h"
+
+namespace cpattn {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBK = 64;          // keys per KV tile
+constexpr int kRowsPerWave = 32;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* qpos;
+  void* o;
+  float* lse;
+  int B, S, Sq, Hq, Hkv, G, cp, c, rank;
+  int hpw, wpr, bm, nrb, nhs, n_items, per_xcd;
+  float scale_log2;
+};
+
+// 16-byte-chunk XOR swizzle of an LDS tile row; stays inside aligned groups of 16 (or 8)
+// chunks so it never leaves the row.
+template <int CH>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (CH % 16 == 0) {
+    return ((row & 7) << 1) | ((row >> 3) & 1);
+  } else {
+    return ((row & 3) << 1) | ((row >> 2) & 1);
+  }
+}
+
+__device__ __forceinline__ float wave_max32(float x) {
+  // max with the lane 32 away (both halves end with the same value)
+  auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+
+__device__ __forceinline__ float wave_sum32(float x) {
+  auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
+
+__device__ __forceinline__ int wave_min_i(int x) {
+  for (int off = 32; off >= 1; off >>= 1) x = min(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+  for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off));
+  return x;
+}
+
+struct WorkItem {
+  int b, g, head0, row_blk;
+};
+
+__device__ __forceinline__ bool decode_item(const FwdParams& p, WorkItem& w) {
+  int bid = blockIdx.x;
+  int xcd = bid % kNumXcd;
+  int slot = bid / kNumXcd;
+  int W = xcd * p.per_xcd + slot;
+  if (W >= p.n_items) return false;
+  int hs = W % p.nhs;
+  int t = W / p.nhs;
+  int rb_desc = t % p.nrb;
+  t /= p.nrb;
+  w.g = t % p.Hkv;
+  w.b = t / p.Hkv;
+  w.row_blk = p.nrb - 1 - rb_desc;  // heavy first: later rows hold later positions
+  w.head0 = w.g * p.G + hs * p.hpw;
+  return true;
+}
+
+// Shared prologue: the row positions of this lane and the workgroup's [qmin, qmax].
+__device__ __forceinline__ void row_positions(const FwdParams& p, const WorkItem& w, int wave, int lane,
+                                              int& my_row, int& my_pos, int& qmin, int& qmax,
+                                              int* s_red) {
+  int row0 = w.row_blk * p.bm + (wave % p.wpr) * kRowsPerWave;
+  my_row = row0 + (lane & 31);
+  bool valid = my_row < p.Sq;
+  int pos = -1;
+  if (valid) {
+    if (p.qpos) {
+      pos = p.qpos[my_row];
+    } else {
+      pos = (int)lb_src((int64_t)p.rank * 2 * p.c + my_row, p.c, p.cp);
+    }
+    pos = min(pos, p.S - 1);
+  }
+  my_pos = pos;
+  int vmin = valid ? pos : 0x7fffffff;
+  int vmax = valid ? pos : -1;
+  vmin = wave_min_i(vmin);
+  vmax = wave_max_i(vmax);
+  if (lane == 0) {
+    s_red[wave] = vmin;
+    s_red[kWaves + wave] = vmax;
+  }
+  __syncthreads();
+  qmin = 0x7fffffff;
+  qmax = -1;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    qmin = min(qmin, s_red[i]);
+    qmax = max(qmax, s_red[kWaves + i]);
+  }
+}
+
+// Tile cursor over the visible keys: chunks 0..imax in original order, 64-key tiles inside.
+struct TileCursor {
+  int chunk, t0;
+};
+
+__device__ __forceinline__ void next_tile(TileCursor& tc, int c, int qmax) {
+  tc.t0 += kBK;
+  if (tc.t0 >= c || tc.chunk * c + tc.t0 > qmax) {
+    tc.chunk += 1;
+    tc.t0 = 0;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16 kernel
+// ------------------------------------------------------------------------------------------
+template <int DQK, int DV>
+struct Bf16Cfg {
+  static constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
+  static constexpr int VCH = DV / 8;
+  static constexpr int K_BYTES = kBK * KCH * 16;
+  static constexpr int V_BYTES = kBK * VCH * 16;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int K_LOADS = kBK * KCH / kThreads;
+  static constexpr int V_LOADS = kBK * VCH / kThreads;
+  static_assert(kBK * KCH % kThreads == 0 && kBK * VCH % kThreads == 0, "tile/thread mismatch");
+  static constexpr int QK_STEPS = DQK / 16;
+  static constexpr int MV = DV / 32;
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p) {
+  using C = Bf16Cfg<DQK, DV>;
+  __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGE];
+  __shared__ int s_red[2 * kWaves];
+
+  WorkItem w;
+  if (!decode_item(p, w)) return;
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int hl = lane / 32;  // which half of the wave
+  const int head = w.head0 + wave / p.wpr;
+
+  int my_row, my_pos, qmin, qmax;
+  row_positions(p, w, wave, lane, my_row, my_pos, qmin, qmax, s_red);
+  if (qmax < 0) return;  // no valid row (cannot happen for a non-empty block)
+
+  const __bf16* qg = static_cast<const __bf16*>(p.q);
+  const __bf16* kg = static_cast<const __bf16*>(p.k);
+  const __bf16* vg = static_cast<const __bf16*>(p.v);
+
+  // Q fragment (B operand of S^T = K Q^T): lane holds row (lane&31), dims 16ks + 8hl .. +7
+  bf16x8 qf[C::QK_STEPS];
+  {
+    int row = my_row < p.Sq ? my_row : p.Sq - 1;
+    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
+        qg + (((int64_t)w.b * p.Sq + row) * p.Hq + head) * DQK);
+#pragma unroll
+    for (int ks = 0; ks < C::QK_STEPS; ++ks) qf[ks] = qrow[2 * ks + hl];
+  }
+
+  const int64_t kv_row_elems_k = (int64_t)p.Hkv * DQK;
+  const int64_t kv_row_elems_v = (int64_t)p.Hkv * DV;
+  const __bf16* kbase = kg + (int64_t)w.b * p.S * kv_row_elems_k + (int64_t)w.g * DQK;
+  const __bf16* vbase = vg + (int64_t)w.b * p.S * kv_row_elems_v + (int64_t)w.g * DV;
+
+  const int c = p.c;
+  const int imax = min(qmax / c, 2 * p.cp - 1);
+
+  // staging registers for the next tile
+  u32x4 kst[C::K_LOADS];
+  u32x4 vst[C::V_LOADS];
+
+  auto load_tile = [&](const TileCursor& tc) {
+    const int64_t prow0 = lb_chunk_offset(tc.chunk, c, p.cp) + tc.t0;
+    const int nvalid = min(kBK, c - tc.t0);
+#pragma unroll
+    for (int u = 0; u < C::K_LOADS; ++u) {
+      int id = tid + u * kThreads;
+      int row = id / C::KCH, ch = id % C::KCH;
+      if (row < nvalid) {
+        kst[u] = *reinterpret_cast<const u32x4*>(kbase + (prow0 + row) * kv_row_elems_k + ch * 8);
+      } else {
+        kst[u] = u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < C::V_LOADS; ++u) {
+      int id = tid + u * kThreads;
+      int row = id / C::VCH, ch = id % C::VCH;
+      if (row < nvalid) {
+        vst[u] = *reinterpret_cast<const u32x4*>(vbase + (prow0 + row) * kv_row_elems_v + ch * 8);
+      } else {
+        vst[u] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* kb = lds + buf * C::STAGE;
+    char* vb = kb + C::K_BYTES;
+#pragma unroll
+    for (int u = 0; u < C::K_LOADS; ++u) {
+      int id = tid + u * kThreads;
+      int row = id / C::KCH, ch = id % C::KCH;
+      *reinterpret_cast<u32x4*>(kb + row * (C::KCH * 16) + ((ch ^ swz<C::KCH>(row)) * 16)) = kst[u];
+    }
+#pragma unroll
+    for (int u = 0; u < C::V_LOADS; ++u) {
+      int id = tid + u * kThreads;
+      int row = id / C::VCH, ch = id % C::VCH;
+      *reinterpret_cast<u32x4*>(vb + row * (C::VCH * 16) + ((ch ^ swz<C::VCH>(row)) * 16)) = vst[u];
+    }
+  };
+
+  f32x16 oacc[C::MV];
+#pragma unroll
+  for (int mv = 0; mv < C::MV; ++mv) oacc[mv] = f32x16{};
+  float m_run = -INFINITY;  // running max, log2 units (scaled logits)
+  float l_part = 0.f;       // this lane's share of the row sum
+
+  const float sl2 = p.scale_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  TileCursor tc{0, 0};
+  load_tile(tc);
+  store_tile(0);
+  __syncthreads();
+  int buf = 0;
+
+  // per-lane transposed-read geometry for V (ds_read_b64_tr_b16): in each 16-lane group,
+  // input lane 4e+q supplies row e, columns 4q..4q+3 of a 4x16 block; output lane j then holds
+  // column j, rows 0..3.
+  const int grp = lane / 16;
+  const int tr_e = (lane % 16) / 4;
+  const int tr_q = lane % 4;
+
+  while (tc.chunk <= imax) {
+    TileCursor nx = tc;
+    next_tile(nx, c, qmax);
+    const bool has_next = nx.chunk <= imax;
+    if (has_next) load_tile(nx);
+
+    const char* kb = lds + buf * C::STAGE;
+    const char* vb = kb + C::K_BYTES;
+
+    // ---- S^T = K Q^T for 64 keys (two 32-key blocks)
+    f32x16 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 acc = {};
+      const int krow = mb * 32 + (lane & 31);
+      const char* kr = kb + krow * (C::KCH * 16);
+      const int sw = swz<C::KCH>(krow);
+#pragma unroll
+      for (int ks = 0; ks < C::QK_STEPS; ++ks) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + (((2 * ks + hl) ^ sw) * 16));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], acc, 0, 0, 0);
+      }
+      s[mb] = acc;
+    }
+
+    // ---- mask (only tiles that reach past the smallest query position, or partial tiles)
+    const int kpos0 = tc.chunk * c + tc.t0;
+    const int nvalid = min(kBK, c - tc.t0);
+    const bool need_mask = (kpos0 + kBK - 1 > qmin) || (nvalid < kBK);
+    if (need_mask) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int kk = mb * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
+          bool vis = (kk < nvalid) && (kpos0 + kk <= my_pos);
+          s[mb][r] = vis ? s[mb][r] : -INFINITY;
+        }
+      }
+    }
+
+    // ---- online softmax (row = lane & 31; this lane holds 32 of the row's 64 scores)
+    float mt = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[1][r]);
+    mt = wave_max32(mt) * sl2;
+    const bool raise = mt > m_run + kRescaleSlack;
+    if (__any(raise)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int mv = 0; mv < C::MV; ++mv) oacc[mv] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+    // probabilities -> bf16 B operands (k-step ks uses registers 8*(ks%2).. of block ks/2)
+    bf16x8 pb[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], sl2, -m_use));
+        float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r + 1], sl2, -m_use));
+        bf16x2 pr = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){e0, e1}, bf16x2);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_part, false);
+        const int ks = mb * 2 + r / 8;
+        const int t = r % 8;
+        pb[ks][t] = pr[0];
+        pb[ks][t + 1] = pr[1];
+      }
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int mv = 0; mv < C::MV; ++mv) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int row_a = 16 * ks + 4 * (grp / 2) + tr_e;
+        const int col = 32 * mv + 16 * (grp % 2) + 4 * tr_q;
+        const int ch = col / 8, within = (col % 8) * 2;
+        const char* pa = vb + row_a * (C::VCH * 16) + ((ch ^ swz<C::VCH>(row_a)) * 16) + within;
+        const int row_b = row_a + 8;
+        const char* pb2 = vb + row_b * (C::VCH * 16) + ((ch ^ swz<C::VCH>(row_b)) * 16) + within;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(pa));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(pb2));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        bf16x8 a = __builtin_bit_cast(bf16x8, cat);
+        oacc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[mv], 0, 0, 0);
+      }
+    }
+
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    tc = nx;
+  }
+
+  // ---- epilogue: O = O / l, LSE = (m + log2 l) * ln 2
+  const float l_tot = wave_sum32(l_part);
+  const float inv_l = 1.f / l_tot;
+  if (my_row < p.Sq) {
+    __bf16* og = static_cast<__bf16*>(p.o) + (((int64_t)w.b * p.Sq + my_row) * p.Hq + head) * DV;
+#pragma unroll
+    for (int mv = 0; mv < C::MV; ++mv) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[mv][a4 * 4 + e] * inv_l);
+        *reinterpret_cast<bf16x4*>(og + 32 * mv + 8 * a4 + 4 * hl) = ov;
+      }
+    }
+    if (p.lse && hl == 0) {
+      p.lse[((int64_t)w.b * p.Hq + head) * p.Sq + my_row] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// fp32 kernel (same schedule; v_mfma_f32_32x32x2_f32, probabilities kept in fp32)
+// ------------------------------------------------------------------------------------------
+template <int D>
+struct F32Cfg {
+  static constexpr int LD = D + 1;  // padded LDS row (floats): odd stride spreads banks
+  static constexpr int TILE = kBK * LD;  // floats per K or V tile
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int CH = D / 4;  // 16-byte chunks per row in global memory
+  static constexpr int LOADS = kBK * CH / kThreads;
+  static_assert(kBK * CH % kThreads == 0, "tile/thread mismatch");
+  static constexpr int QK_STEPS = D / 2;
+  static constexpr int MV = D / 32;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(FwdParams p) {
+  using C = F32Cfg<D>;
+  __shared__ float lds[2 * C::STAGE];
+  __shared__ int s_red[2 * kWaves];
+
+  WorkItem w;
+  if (!decode_item(p, w)) return;
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int hl = lane / 32;
+  const int head = w.head0 + wave / p.wpr;
+
+  int my_row, my_pos, qmin, qmax;
+  row_positions(p, w, wave, lane, my_row, my_pos, qmin, qmax, s_red);
+  if (qmax < 0) return;
+
+  const float* qg = static_cast<const float*>(p.q);
+  const float* kg = static_cast<const float*>(p.k);
+  const float* vg = static_cast<const float*>(p.v);
+
+  float qf[C::QK_STEPS];
+  {
+    int row = my_row < p.Sq ? my_row : p.Sq - 1;
+    const float* qrow = qg + (((int64_t)w.b * p.Sq + row) * p.Hq + head) * D;
+#pragma unroll
+    for (int ks = 0; ks < C::QK_STEPS; ++ks) qf[ks] = qrow[2 * ks + hl];
+  }
+
+  const int64_t kv_row = (int64_t)p.Hkv * D;
+  const float* kbase = kg + (int64_t)w.b * p.S * kv_row + (int64_t)w.g * D;
+  const float* vbase = vg + (int64_t)w.b * p.S * kv_row + (int64_t)w.g * D;
+  const int c = p.c;
+  const int imax = min(qmax / c, 2 * p.cp - 1);
+
+  f32x4 kst[C::LOADS];
+  f32x4 vst[C::LOADS];
+  auto load_tile = [&](const TileCursor& tc) {
+    const int64_t prow0 = lb_chunk_offset(tc.chunk, c, p.cp) + tc.t0;
+    const int nvalid = min(kBK, c - tc.t0);
+#pragma unroll
+    for (int u = 0; u < C::LOADS; ++u) {
+      int id = tid + u * kThreads;
+      int row = id / C::CH, ch = id % C::CH;
+      if (row < nvalid) {
+        kst[u] = *reinterpret_cast<const f32x4*>(kbase + (prow0 + row) * kv_row + ch * 4);
+        vst[u] = *reinterpret_cast<const f32x4*>(vbase + (prow0 + row) * kv_row + ch * 4);
+      } else {
+        kst[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        vst[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  auto store_tile = [&](int b) {
+    float* kb = lds + b * C::STAGE;
+    float* vb = kb + C::TILE;
+#pragma unroll
+    for (int u = 0; u < C::LOADS; ++u) {
+      int id = tid + u * kThreads;
+      int row = id / C::CH, ch = id % C::CH;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kb[row * C::LD + ch * 4 + e] = kst[u][e];
+        vb[row * C::LD + ch * 4 + e] = vst[u][e];
+      }
+    }
+  };
+
+  f32x16 oacc[C::MV];
+#pragma unroll
+  for (int mv = 0; mv < C::MV; ++mv) oacc[mv] = f32x16{};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+  const float sl2 = p.scale_log2;
+
+  TileCursor tc{0, 0};
+  load_tile(tc);
+  store_tile(0);
+  __syncthreads();
+  int buf = 0;
+
+  while (tc.chunk <= imax) {
+    TileCursor nx = tc;
+    next_tile(nx, c, qmax);
+    const bool has_next = nx.chunk <= imax;
+    if (has_next) load_tile(nx);
+    const float* kb = lds + buf * C::STAGE;
+    const float* vb = kb + C::TILE;
+
+    f32x16 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 acc = {};
+      const float* kr = kb + (mb * 32 + (lane & 31)) * C::LD;
+#pragma unroll
+      for (int ks = 0; ks < C::QK_STEPS; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[2 * ks + hl], qf[ks], acc, 0, 0, 0);
+      }
+      s[mb] = acc;
+    }
+
+    const int kpos0 = tc.chunk * c + tc.t0;
+    const int nvalid = min(kBK, c - tc.t0);
+    const bool need_mask = (kpos0 + kBK - 1 > qmin) || (nvalid < kBK);
+    if (need_mask) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int kk = mb * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
+          bool vis = (kk < nvalid) && (kpos0 + kk <= my_pos);
+          s[mb][r] = vis ? s[mb][r] : -INFINITY;
+        }
+      }
+    }
+
+    float mt = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[1][r]);
+    mt = wave_max32(mt) * sl2;
+    const bool raise = mt > m_run + kRescaleSlack;
+    if (__any(raise)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int mv = 0; mv < C::MV; ++mv) oacc[mv] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], sl2, -m_use));
+        s[mb][r] = e;
+        l_part += e;
+      }
+    }
+
+    // O^T += V^T P^T: MFMA (mb, r) pairs key 32mb + 8(r/4) + 4*half + r%4 with that P register
+#pragma unroll
+    for (int mv = 0; mv < C::MV; ++mv) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = mb * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
+          float a = vb[key * C::LD + 32 * mv + (lane & 31)];
+          oacc[mv] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[mb][r], oacc[mv], 0, 0, 0);
+        }
+      }
+    }
+
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    tc = nx;
+  }
+
+  const float l_tot = wave_sum32(l_part);
+  const float inv_l = 1.f / l_tot;
+  if (my_row < p.Sq) {
+    float* og = static_cast<float*>(p.o) + (((int64_t)w.b * p.Sq + my_row) * p.Hq + head) * D;
+#pragma unroll
+    for (int mv = 0; mv < C::MV; ++mv) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        f32x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = oacc[mv][a4 * 4 + e] * inv_l;
+        *reinterpret_cast<f32x4*>(og + 32 * mv + 8 * a4 + 4 * hl) = ov;
+      }
+    }
+    if (p.lse && hl == 0) {
+      p.lse[((int64_t)w.b * p.Hq + head) * p.Sq + my_row] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+  }
+}
+
+int gcd_int(int a, int b) {
+  while (b) {
+    int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+FwdParams make_params(const AttnArgs& a) {
+  FwdParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.qpos = a.q_pos;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.B = a.batch;
+  p.S = a.seq;
+  p.Sq = a.sq;
+  p.Hq = a.hq;
+  p.Hkv = a.hkv;
+  p.G = a.hq / a.hkv;
+  p.cp = a.cp;
+  p.c = a.seq / (2 * a.cp);
+  p.rank = a.rank;
+  p.hpw = gcd_int(p.G, kWaves);
+  p.wpr = kWaves / p.hpw;
+  p.bm = kRowsPerWave * p.wpr;
+  p.nrb = (p.Sq + p.bm - 1) / p.bm;
+  p.nhs = p.G / p.hpw;
+  p.n_items = p.B * p.Hkv * p.nrb * p.nhs;
+  p.per_xcd = (p.n_items + kNumXcd - 1) / kNumXcd;
+  p.scale_log2 = a.scale * kLog2e;
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
+  FwdParams p = make_params(a);
+  if (p.n_items == 0) return hipSuccess;
+  dim3 grid(p.per_xcd * kNumXcd), block(kThreads);
+  if (a.d_qk == 128 && a.d_v == 128) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 128>), grid, block, 0, stream, p);
+  } else if (a.d_qk == 64 && a.d_v == 64) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 64>), grid, block, 0, stream, p);
+  } else if (a.d_qk == 192 && a.d_v == 128) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<192, 128>), grid, block, 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream) {
+  FwdParams p = make_params(a);
+  if (p.n_items == 0) return hipSuccess;
+  dim3 grid(p.per_xcd * kNumXcd), block(kThreads);
+  if (a.d_qk == 64 && a.d_v == 64) {
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<64>), grid, block, 0, stream, p);
+  } else if (a.d_qk == 128 && a.d_v == 128) {
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<128>), grid, block, 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

@@ -1,0 +1,74 @@
+// Shared helpers of the gfx950 kernels: vector types, the load-balance index, launcher
+// declarations. Internal to libcpattn.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Load-balanced order ("Add context parallelism", PR 1445, Description): 2*cp chunks of c
+// tokens; rank r holds chunk r then chunk 2cp-1-r, ranks concatenated in order. Permuted slot j
+// therefore holds original position src(j).
+__host__ __device__ inline int64_t lb_src(int64_t j, int64_t c, int64_t cp) {
+  int64_t r = j / (2 * c);
+  int64_t w = j - r * 2 * c;
+  return w < c ? r * c + w : (2 * cp - 1 - r) * c + (w - c);
+}
+
+// Permuted row offset of original chunk i (the inverse map at chunk granularity): chunk i < cp
+// is the first half of rank i's shard; chunk i >= cp is the second half of rank 2cp-1-i's.
+__host__ __device__ inline int64_t lb_chunk_offset(int64_t i, int64_t c, int64_t cp) {
+  return i < cp ? i * 2 * c : (2 * cp - 1 - i) * 2 * c + c;
+}
+
+// Number of XCDs on MI355X: consecutive workgroup ids are dealt round-robin to them, and each
+// has its own L2.
+constexpr int kNumXcd = 8;
+
+// ---- launchers (defined in the .hip files; return the launch status) ----
+hipError_t launch_permute(const void* src, void* dst, int64_t outer, int64_t seq, int64_t row_bytes,
+                          int64_t cp, int64_t row_begin, int64_t row_count, bool scatter,
+                          hipStream_t stream);
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* q_pos;  // may be null: positions from (cp, rank)
+  void* o;
+  float* lse;            // may be null
+  int batch, seq, sq, hq, hkv, d_qk, d_v, cp, rank;
+  float scale;
+};
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* lengths;
+  void* o;
+  float* lse;
+  float* ws;
+  int batch, hq, hkv, d, max_len, nsplit, split_len;
+  float scale;
+};
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+
+// Decode split geometry shared by the workspace-size query and the launcher.
+constexpr int kDecodeSplitLen = 256;
+inline int decode_nsplit(int max_len) { return (max_len + kDecodeSplitLen - 1) / kDecodeSplitLen; }
+
+}  // namespace cpattn

@@ -1,0 +1,161 @@
+/*
+ * cpattn.h - C ABI of libcpattn.so: load-balanced context-parallel causal attention and
+ * grouped-query decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions for every call below
+ *  - Pointers named for tensors are DEVICE pointers (hipMalloc'd or torch CUDA storage) unless
+ *    the comment says host. The caller owns every buffer; the library allocates nothing per call
+ *    and keeps no pointer after it returns.
+ *  - Tensors are dense, row-major, innermost dimension last, with the shapes given.
+ *  - Calls that take `stream` enqueue work on that hipStream_t (NULL = the null stream) and
+ *    return without synchronising. Results are ready when the stream reaches that point.
+ *  - Every shape, dtype, alignment and pointer check runs on the host before any HIP call.
+ *    A failed check returns CPA_EINVAL (bad argument) or CPA_ENOTSUP (valid but unsupported
+ *    combination, or a device that is not gfx950) and enqueues nothing. A HIP launch or runtime
+ *    failure returns CPA_EHIP. cpattn_last_error() then gives a message for the calling thread.
+ *  - Preconditions that live in device memory (position and length values) cannot be checked
+ *    without a synchronisation. Kernels clamp them so that no access leaves the buffers, but
+ *    the numbers produced for out-of-range values are unspecified.
+ *  - Batch 0, zero rows or zero sequences are valid and enqueue nothing.
+ *
+ * Load-balanced order ("Add context parallelism", MaxText PR 1445, Description): the sequence
+ * of length S is cut into 2*cp chunks of c = S/(2*cp) tokens; rank r keeps chunk r followed by
+ * chunk 2*cp-1-r, so every rank sees about the same number of causal (query, key) pairs. For
+ * cp = 2 and S = 8 this gives 0,1,6,7 | 2,3,4,5. The "permuted" sequence is the concatenation of
+ * the ranks' shards in rank order, which is what an all-gather of the shards returns. Permuted
+ * slot j holds original position src(j) = r*c + w if w < c, else (2*cp-1-r)*c + (w-c), where
+ * r = j / (2c), w = j % (2c).
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CPA_OK = 0,
+  CPA_EINVAL = -22,   /* an argument is invalid (shape, divisibility, null or misaligned pointer) */
+  CPA_ENOTSUP = -95,  /* valid but unsupported here (head dim, dtype, device other than gfx950)  */
+  CPA_EHIP = -1000    /* a HIP runtime call or kernel launch failed                              */
+} cpa_status;
+
+typedef enum {
+  CPA_F32 = 0,   /* IEEE float32 storage, float32 arithmetic                                 */
+  CPA_BF16 = 1   /* bfloat16 storage, float32 accumulation                                   */
+} cpa_dtype;
+
+/* Message for the last non-OK status returned on the calling thread (never NULL). */
+const char* cpattn_last_error(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * Index helpers (host only, no HIP call).
+ * ------------------------------------------------------------------------------------------- */
+
+/* Original token position held by permuted slot j, i.e. src(j) above.
+ * Returns -1 if seq < 1, cp < 1, seq % (2*cp) != 0 or j is outside [0, seq). */
+int64_t cp_load_balance_source_index(int64_t seq, int32_t cp, int64_t j);
+
+/* Writes src(row_begin + i) for i in [0, row_count) to out_host (HOST int32 array of row_count
+ * entries). Rank r's query positions are row_begin = r*2c, row_count = 2c.
+ * CPA_EINVAL for the same conditions as above, for a window outside [0, seq), or seq >= 2^31. */
+int cp_load_balance_positions(int64_t seq, int32_t cp, int64_t row_begin, int64_t row_count,
+                              int32_t* out_host);
+
+/* ---------------------------------------------------------------------------------------------
+ * Load-balance permutation: the token reorder that "Add context parallelism" (PR 1445,
+ * Description) performs with a gather along the sequence axis. Both calls are bit copies: rows
+ * are moved as raw bytes, so any dtype works and the round trip is exact.
+ *
+ * A tensor is viewed as [outer, seq, row_bytes]: every dimension before the sequence axis folds
+ * into `outer`, every dimension after it into `row_bytes` (e.g. Q [B,S,H,D] bf16 has outer = B,
+ * row_bytes = H*D*2; an LSE [B,H,S] fp32 permuted along S has outer = B*H, row_bytes = 4).
+ * The window [row_begin, row_begin + row_count) selects slots of the PERMUTED order; the full
+ * permutation is row_begin = 0, row_count = seq. A rank's own share is row_begin = r*2c,
+ * row_count = 2c.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Gather. src: [outer, seq, row_bytes] in original token order.
+ * dst: [outer, row_count, row_bytes]; dst[o, i] = src[o, src(row_begin + i)].
+ * src and dst must not overlap. CPA_EINVAL if seq % (2*cp) != 0, cp < 1, the window leaves
+ * [0, seq), row_bytes < 1, or a pointer is NULL while the copy is non-empty. */
+int cp_load_balance_permute(const void* src, void* dst, int64_t outer, int64_t seq,
+                            int64_t row_bytes, int32_t cp, int64_t row_begin, int64_t row_count,
+                            void* stream);
+
+/* Scatter, the exact inverse. src: [outer, row_count, row_bytes] holding permuted slots
+ * [row_begin, row_begin + row_count). dst: [outer, seq, row_bytes] in original order;
+ * dst[o, src(row_begin + i)] = src[o, i]. Rows of dst outside the window's images are left
+ * untouched, so calling it once per rank (or once with the full window) rebuilds the whole
+ * tensor. Same errors as cp_load_balance_permute. */
+int cp_load_balance_unpermute(const void* src, void* dst, int64_t outer, int64_t seq,
+                              int64_t row_bytes, int32_t cp, int64_t row_begin, int64_t row_count,
+                              void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Causal grouped-query attention forward for one context-parallel rank ("Add context
+ * parallelism", PR 1445, Description: keys and values all-gathered, queries sharded on the
+ * sequence, tokens and mask reordered for balance; unit test of "Add support for EP to context
+ * parallelism in self-attention", PR 2023: the sharded result equals un-sharded dot-product
+ * attention).
+ *
+ *   q_shard     [B, sq, Hq, Dqk]  the rank's query rows (in its shard order)
+ *   k           [B, seq, Hkv, Dqk] all keys in PERMUTED (all-gathered) order
+ *   v           [B, seq, Hkv, Dv]  all values in permuted order
+ *   q_positions [sq] int32, original position of each query row; NULL means the rank's own
+ *               shard, src(rank*2c + i), in which case sq must equal 2c = seq/cp
+ *   o           [B, sq, Hq, Dv] same dtype as q (output)
+ *   lse         [B, Hq, sq] float32 (output, may be NULL): natural-log log-sum-exp of the scaled
+ *               logits of each row
+ *
+ * For row i and query head h (kv head g = h / (Hq/Hkv)), key j is visible iff
+ * src(j) <= q_positions[i] (a token sees itself):
+ *   O[b,i,h,:] = sum_j softmax_j(scale * q.k_j) * v_j,  LSE[b,h,i] = ln sum_j exp(scale*q.k_j).
+ * Precision: float32 accumulation; for bf16 the probabilities are rounded to bf16 before the PV
+ * product and the row sum uses the same rounded values.
+ * Supported (dtype, Dqk, Dv): bf16 with (64,64), (128,128), (192,128); f32 with (64,64),
+ * (128,128). Others return CPA_ENOTSUP.
+ * CPA_EINVAL if seq % (2*cp) != 0, rank outside [0, cp), hq % hkv != 0, a needed pointer is NULL
+ * or not 16-byte aligned, scale is not finite and positive, or q_positions == NULL with
+ * sq != seq/cp. Device precondition: 0 <= q_positions[i] < seq. */
+int cp_attention_fwd(const void* q_shard, const void* k, const void* v,
+                     const int32_t* q_positions, void* o, float* lse,
+                     int32_t batch, int32_t seq, int32_t sq, int32_t hq, int32_t hkv,
+                     int32_t d_qk, int32_t d_v, int32_t dtype, float softmax_scale,
+                     int32_t cp, int32_t rank, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Grouped-query single-token decode attention ("Add Pallas GPU decode attention in Maxtext
+ * inference", PR 1066, Description: decode calls a grouped-query attention kernel; Tests: the
+ * cache is filled by a prefill and grows to the target length). The newest token attends to
+ * cache entries 0 .. lengths[b]-1 of its sequence. Split-K over the cache length: a first kernel
+ * writes per-split (max, sum, unnormalised output) partials into `workspace`, a second merges
+ * them with log-sum-exp weights.
+ *
+ *   q        [B, Hq, D]
+ *   k_cache  [B, Hkv, max_len, D]   (each (b, kv head) slab contiguous)
+ *   v_cache  [B, Hkv, max_len, D]
+ *   lengths  [B] int32 (device), valid entries per sequence; device precondition
+ *            1 <= lengths[b] <= max_len. Entries at index >= lengths[b] are never read.
+ *   o        [B, Hq, D] same dtype as q (output)
+ *   lse      [B, Hq] float32 (output, may be NULL)
+ *   workspace, workspace_bytes: device scratch of at least gqa_decode_workspace_bytes(...)
+ *            bytes, owned by the caller; its contents on entry do not matter.
+ * Supported: bf16 and f32 with D in {64, 128}. CPA_EINVAL for hq % hkv != 0, null or misaligned
+ * pointers, a workspace that is too small, or a non-positive scale. */
+size_t gqa_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t max_len, int32_t d);
+
+int gqa_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* lengths, void* o, float* lse,
+                         int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t max_len,
+                         int32_t dtype, float softmax_scale,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

@@ -25,12 +25,13 @@ float64).
 """
 
 import numpy as np
+import torch
 
 from .lb_index import load_balance_perm
 
 
 def _f64(x):
-    """Exact upcast of a numpy array or a CPU torch tensor (any float dtype) to float64."""
+    """Exact upcast of a numpy array or a CPU torch tensor (any float dtype) to float64 numpy."""
     if hasattr(x, "detach"):  # torch tensor
         import torch
 
@@ -38,29 +39,37 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
+def _t64(x):
+    """Exact upcast to a float64 CPU torch tensor (shares memory with float64 numpy input)."""
+    if hasattr(x, "detach"):
+        return x.detach().to(device="cpu", dtype=torch.float64)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+
+
 def causal_attention_ref(q, k, v, q_pos, k_pos, scale, rows=None, row_block=256):
     """Masked two-pass softmax attention with grouped-query heads.
 
-    q: [B, Sq, Hq, Dqk]; k: [B, Sk, Hkv, Dqk]; v: [B, Sk, Hkv, Dv] (any float dtype).
-    q_pos: [Sq] original positions of the query rows; k_pos: [Sk] original positions of the
-    key rows. A key j is visible to row i iff ``k_pos[j] <= q_pos[i]``.
+    q: [B, Sq, Hq, Dqk]; k: [B, Sk, Hkv, Dqk]; v: [B, Sk, Hkv, Dv] (any float dtype, numpy or
+    CPU torch). q_pos: [Sq] original positions of the query rows; k_pos: [Sk] original
+    positions of the key rows. A key j is visible to row i iff ``k_pos[j] <= q_pos[i]``.
     rows: optional iterable of query-row indices; only those rows are computed (the rest of
     the returned arrays are NaN).
 
-    Returns (O [B, Sq, Hq, Dv] float64, LSE [B, Hq, Sq] float64).
+    The arithmetic is float64 torch CPU ops (matmul, exp, max, sum), one (batch, query head)
+    at a time. Returns (O [B, Sq, Hq, Dv] float64, LSE [B, Hq, Sq] float64) as numpy arrays.
     """
-    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    q64, k64, v64 = _t64(q), _t64(k), _t64(v)
     B, Sq, Hq, _ = q64.shape
     Sk, Hkv, Dv = k64.shape[1], k64.shape[2], v64.shape[3]
     if Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
-    q_pos = np.asarray(q_pos, dtype=np.int64)
-    k_pos = np.asarray(k_pos, dtype=np.int64)
-    row_ids = np.arange(Sq) if rows is None else np.unique(np.asarray(rows, dtype=np.int64))
+    q_pos = torch.as_tensor(np.asarray(q_pos, dtype=np.int64))
+    k_pos = torch.as_tensor(np.asarray(k_pos, dtype=np.int64))
+    row_ids = torch.arange(Sq) if rows is None else torch.as_tensor(np.unique(np.asarray(rows, dtype=np.int64)))
 
-    out = np.full((B, Sq, Hq, Dv), np.nan)
-    lse = np.full((B, Hq, Sq), np.nan)
+    out = torch.full((B, Sq, Hq, Dv), float("nan"), dtype=torch.float64)
+    lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float64)
     for b in range(B):
         for g in range(Hkv):
             kg = k64[b, :, g, :]
@@ -69,18 +78,18 @@ def causal_attention_ref(q, k, v, q_pos, k_pos, scale, rows=None, row_block=256)
                 blk = row_ids[start:start + row_block]
                 qp = q_pos[blk]
                 # keys that can be visible to any row of the block (a selection, not a reorder)
-                cand = np.nonzero(k_pos <= qp.max())[0]
+                cand = torch.nonzero(k_pos <= qp.max()).flatten()
                 visible = k_pos[cand][None, :] <= qp[:, None]
                 kc, vc = kg[cand], vg[cand]
                 for h in range(g * G, (g + 1) * G):
                     s = scale * (q64[b, blk, h, :] @ kc.T)
-                    s = np.where(visible, s, -np.inf)
-                    m = s.max(axis=1)
-                    p = np.exp(s - m[:, None])
-                    l = p.sum(axis=1)
+                    s = torch.where(visible, s, float("-inf"))
+                    m = s.max(dim=1).values
+                    p = torch.exp(s - m[:, None])
+                    l = p.sum(dim=1)
                     out[b, blk, h, :] = (p @ vc) / l[:, None]
-                    lse[b, h, blk] = m + np.log(l)
-    return out, lse
+                    lse[b, h, blk] = m + torch.log(l)
+    return out.numpy(), lse.numpy()
 
 
 def cp_attention_ref(q_shard, k_perm, v_perm, q_positions, seq, cp, scale, rows=None):

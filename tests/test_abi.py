@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, its host
+index helper agrees with the oracle's independent construction, and every argument check
+fails with the documented status before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import context_causal_attention_load_amd as cpa
+from context_causal_attention_load_amd import binding
+from oracle import lb_index as olb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cpa.library_path()):
+        from context_causal_attention_load_amd import build
+
+        build.build()
+    return cpa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("cp_load_balance_permute", "cp_load_balance_unpermute", "cp_attention_fwd",
+                 "gqa_decode_attention", "gqa_decode_workspace_bytes", "cpattn_last_error",
+                 "cp_load_balance_source_index", "cp_load_balance_positions"):
+        assert must in names, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(cpa.library_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), f"missing export {name}"
+
+
+@pytest.mark.parametrize("seq,cp", [(8, 1), (8, 2), (8, 4), (96, 3), (512, 2), (8192, 4), (131072, 8)])
+def test_source_index_matches_oracle(lib, seq, cp):
+    perm = olb.load_balance_perm(seq, cp)
+    got = cpa.lb_positions(seq, cp).numpy()
+    assert np.array_equal(got, perm)
+    for r in range(cp):
+        b0, b1 = olb.shard_row_range(seq, cp, r)
+        assert np.array_equal(cpa.lb_positions(seq, cp, b0, b1 - b0).numpy(), olb.shard_positions(seq, cp, r))
+    for j in (0, seq // 2, seq - 1):
+        assert cpa.lb_source_index(seq, cp, j) == perm[j]
+
+
+def test_source_index_rejects(lib):
+    assert lib.cp_load_balance_source_index(10, 2, 0) == -1
+    assert lib.cp_load_balance_source_index(8, 0, 0) == -1
+    assert lib.cp_load_balance_source_index(8, 2, 8) == -1
+    assert lib.cp_load_balance_source_index(8, 2, -1) == -1
+
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails its host checks first
+
+
+def _status_and_message(lib, rc):
+    return rc, lib.cpattn_last_error().decode()
+
+
+@pytest.mark.parametrize("args,substr", [
+    ((FAKE, ctypes.c_void_p(1 << 20), 1, 10, 16, 2, 0, 10, None), "multiple of 2*cp"),
+    ((FAKE, ctypes.c_void_p(1 << 20), 1, 8, 16, 0, 0, 8, None), "cp must be"),
+    ((FAKE, ctypes.c_void_p(1 << 20), 1, 8, 0, 2, 0, 8, None), "row_bytes"),
+    ((FAKE, ctypes.c_void_p(1 << 20), 1, 8, 16, 2, 4, 8, None), "window"),
+    ((FAKE, ctypes.c_void_p(1 << 20), 1, 8, 16, 2, -1, 2, None), "window"),
+    ((None, ctypes.c_void_p(1 << 20), 1, 8, 16, 2, 0, 8, None), "null"),
+    ((FAKE, ctypes.c_void_p(4096 + 64), 1, 8, 16, 2, 0, 8, None), "overlap"),
+    ((FAKE, ctypes.c_void_p(1 << 20), -1, 8, 16, 2, 0, 8, None), "outer"),
+])
+def test_permute_argument_errors(lib, args, substr):
+    for fn in (lib.cp_load_balance_permute, lib.cp_load_balance_unpermute):
+        rc, msg = _status_and_message(lib, fn(*args))
+        assert rc == binding.CPA_EINVAL and substr in msg, (rc, msg)
+
+
+def test_permute_empty_is_ok_without_device(lib):
+    assert lib.cp_load_balance_permute(None, None, 0, 8, 16, 2, 0, 8, None) == 0
+    assert lib.cp_load_balance_permute(None, None, 1, 8, 16, 2, 3, 0, None) == 0
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, pos=None, o=ctypes.c_void_p(1 << 30), lse=None, batch=1, seq=512, sq=256,
+             hq=4, hkv=2, dqk=64, dv=64, dtype=binding.CPA_F32, scale=0.125, cp=2, rank=0)
+    a.update(kw)
+    rc = lib.cp_attention_fwd(a["q"], a["k"], a["v"], a["pos"], a["o"], a["lse"], a["batch"], a["seq"], a["sq"],
+                              a["hq"], a["hkv"], a["dqk"], a["dv"], a["dtype"], a["scale"], a["cp"], a["rank"], None)
+    return _status_and_message(lib, rc)
+
+
+@pytest.mark.parametrize("kw,status,substr", [
+    (dict(seq=502), binding.CPA_EINVAL, "multiple of 2*cp"),
+    (dict(rank=2), binding.CPA_EINVAL, "rank"),
+    (dict(rank=-1), binding.CPA_EINVAL, "rank"),
+    (dict(hq=3), binding.CPA_EINVAL, "multiple of hkv"),
+    (dict(scale=0.0), binding.CPA_EINVAL, "softmax_scale"),
+    (dict(scale=float("nan")), binding.CPA_EINVAL, "softmax_scale"),
+    (dict(sq=100), binding.CPA_EINVAL, "without q_positions"),
+    (dict(dtype=7), binding.CPA_EINVAL, "dtype"),
+    (dict(dqk=96, dv=96), binding.CPA_ENOTSUP, "not supported"),
+    (dict(dqk=192, dv=128), binding.CPA_ENOTSUP, "not supported"),  # fp32 has no MLA variant
+    (dict(q=None), binding.CPA_EINVAL, "null"),
+    (dict(k=ctypes.c_void_p(4100)), binding.CPA_EINVAL, "aligned"),
+    (dict(lse=ctypes.c_void_p(4098)), binding.CPA_EINVAL, "lse"),
+    (dict(pos=ctypes.c_void_p(4098), sq=10), binding.CPA_EINVAL, "q_positions"),
+])
+def test_attention_argument_errors(lib, kw, status, substr):
+    rc, msg = _fwd(lib, **kw)
+    assert rc == status and substr in msg, (rc, msg)
+
+
+def test_attention_empty_is_ok_without_device(lib):
+    assert _fwd(lib, batch=0)[0] == 0
+    assert _fwd(lib, sq=0, pos=FAKE)[0] == 0
+
+
+def _dec(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lengths=FAKE, o=FAKE, lse=None, batch=24, hq=48, hkv=8, d=128, max_len=2048,
+             dtype=binding.CPA_BF16, scale=0.088, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    rc = lib.gqa_decode_attention(a["q"], a["k"], a["v"], a["lengths"], a["o"], a["lse"], a["batch"], a["hq"],
+                                  a["hkv"], a["d"], a["max_len"], a["dtype"], a["scale"], a["ws"], a["ws_bytes"], None)
+    return _status_and_message(lib, rc)
+
+
+@pytest.mark.parametrize("kw,status,substr", [
+    (dict(hq=50), binding.CPA_EINVAL, "multiple of hkv"),
+    (dict(max_len=0), binding.CPA_EINVAL, "max_len"),
+    (dict(scale=-1.0), binding.CPA_EINVAL, "softmax_scale"),
+    (dict(d=96), binding.CPA_ENOTSUP, "head dim"),
+    (dict(lengths=None), binding.CPA_EINVAL, "null"),
+    (dict(ws_bytes=16), binding.CPA_EINVAL, "workspace"),
+    (dict(v=ctypes.c_void_p(4104)), binding.CPA_EINVAL, "aligned"),
+    (dict(dtype=3), binding.CPA_EINVAL, "dtype"),
+])
+def test_decode_argument_errors(lib, kw, status, substr):
+    rc, msg = _dec(lib, **kw)
+    assert rc == status and substr in msg, (rc, msg)
+
+
+def test_decode_workspace_size(lib):
+    # (max, sum, D outputs) per (sequence, query head, split of 256 keys)
+    assert cpa.decode_workspace_bytes(24, 48, 8, 2048, 128) == 24 * 48 * 8 * 130 * 4
+    assert cpa.decode_workspace_bytes(1, 1, 1, 1, 64) == 66 * 4
+    assert cpa.decode_workspace_bytes(0, 48, 8, 2048, 128) == 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+
+    with pytest.raises(ValueError):
+        cpa.permute(torch.zeros(1, 8, 4), 2)

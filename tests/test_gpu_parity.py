@@ -1,0 +1,318 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Inputs come from the seeded generators in ``context_causal_attention_load_amd.synth``; the
+oracle permutes and computes from the natural-order CPU tensors on its own, so no oracle input
+or expected value comes from the GPU. Tolerances: max abs error <= 1e-4 for float32 inputs and
+<= 2e-2 for bfloat16 inputs (on O and on LSE); the permutation is compared bit for bit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import context_causal_attention_load_amd as cpa
+from context_causal_attention_load_amd import synth
+from oracle import attention as oatt
+from oracle import lb_index as olb
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+def announce(msg):
+    print(f"\n[gpu case] {msg}", flush=True)
+
+
+def assert_close(got, ref, tol, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    i = np.unravel_index(int(np.argmax(err)), err.shape)
+    print(f"  {what}: max abs err {err.max():.3e} at {i} (tol {tol:g})", flush=True)
+    assert err.max() <= tol, f"{what}: max abs err {err.max():.3e} at {i} > {tol}"
+
+
+def sample_rows(c, n_random, seed):
+    """First/last rows of both chunks of a shard plus seeded random rows (shard has 2c rows)."""
+    edge = list(range(min(4, c))) + list(range(max(0, c - 4), c))
+    edge += [c + x for x in edge]
+    rng = np.random.default_rng(seed)
+    rnd = rng.integers(0, 2 * c, n_random).tolist()
+    return np.unique(np.array(edge + rnd, dtype=np.int64))
+
+
+class Prefill:
+    """Natural-order inputs on host and device, permuted on the device by the library; the
+    oracle permutes the host copies itself."""
+
+    def __init__(self, batch, seq, hq, hkv, dqk, dv, dtype, seed):
+        self.seq, self.dtype = seq, dtype
+        self.q, self.k, self.v = synth.prefill_inputs(batch, seq, hq, hkv, dqk, dv, dtype, seed)
+        self.qd, self.kd, self.vd = (t.to(DEV) for t in (self.q, self.k, self.v))
+        self.scale = 1.0 / math.sqrt(dqk)
+        self._perm = {}
+        self._ref_perm = {}
+
+    def kv_perm(self, cp):
+        if cp not in self._perm:
+            self._perm[cp] = (cpa.permute(self.kd, cp), cpa.permute(self.vd, cp))
+        return self._perm[cp]
+
+    def ref_kv_perm(self, cp):
+        if cp not in self._ref_perm:
+            self._ref_perm = {cp: (oatt.permute_ref(self.k, self.seq, cp).double(),
+                                   oatt.permute_ref(self.v, self.seq, cp).double())}
+        return self._ref_perm[cp]
+
+    def gpu_rank(self, cp, rank, q_positions=None):
+        c = self.seq // (2 * cp)
+        kp, vp = self.kv_perm(cp)
+        qs = cpa.permute(self.qd, cp, row_begin=rank * 2 * c, row_count=2 * c)
+        o, lse = cpa.attention_fwd(qs, kp, vp, cp, rank, q_positions=q_positions, scale=self.scale)
+        torch.cuda.synchronize()
+        return o, lse
+
+    def oracle_rank(self, cp, rank, rows=None):
+        c = self.seq // (2 * cp)
+        qs = oatt.permute_ref(self.q, self.seq, cp, rank * 2 * c, 2 * c)
+        pos = olb.shard_positions(self.seq, cp, rank)
+        kp, vp = self.ref_kv_perm(cp)
+        if rows is not None:
+            qs, pos = qs[:, rows], pos[rows]
+        return oatt.cp_attention_ref(qs, kp, vp, pos, self.seq, cp, self.scale)
+
+
+def check_rank(pf, cp, rank, rows=None, tag=""):
+    announce(f"{tag} attention_fwd cp={cp} rank={rank} rows={'all' if rows is None else len(rows)}")
+    o, lse = pf.gpu_rank(cp, rank)
+    O_ref, L_ref = pf.oracle_rank(cp, rank, rows)
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    if rows is not None:
+        o, lse = o[:, rows], lse[:, :, rows]
+    tol = TOL[pf.dtype]
+    assert_close(o, O_ref, tol, f"{tag} O cp={cp} r={rank}")
+    assert_close(lse, L_ref, tol, f"{tag} LSE cp={cp} r={rank}")
+
+
+# ----------------------------------------------------------------------------- permutation
+
+@pytest.mark.parametrize("outer,seq,inner,dtype,cp", [
+    (1, 512, (4, 64), torch.float32, 2),
+    (2, 96, (3,), torch.int32, 3),
+    (3, 64, (5,), torch.uint8, 4),        # 5-byte rows: byte path
+    (2, 40, (3,), torch.int16, 2),        # 6-byte rows: 2-byte path
+    (1, 4096, (2, 4), torch.bfloat16, 8),  # 16-byte rows
+    (1, 8192, (32, 128), torch.bfloat16, 4),
+])
+def test_permute_bit_exact(outer, seq, inner, dtype, cp):
+    announce(f"permute outer={outer} seq={seq} inner={inner} {dtype} cp={cp}")
+    g = torch.Generator().manual_seed(seq + cp)
+    if dtype.is_floating_point:
+        x = torch.randn((outer, seq) + inner, generator=g).to(dtype)
+    else:
+        info = torch.iinfo(dtype)
+        x = torch.randint(info.min, info.max, (outer, seq) + inner, generator=g, dtype=torch.int64).to(dtype)
+    xd = x.to(DEV)
+    full = cpa.permute(xd, cp).cpu()
+    assert torch.equal(full, oatt.permute_ref(x, seq, cp))
+    c = seq // (2 * cp)
+    back = torch.zeros_like(xd)
+    for r in range(cp):
+        win = cpa.permute(xd, cp, row_begin=r * 2 * c, row_count=2 * c)
+        assert torch.equal(win.cpu(), oatt.permute_ref(x, seq, cp, r * 2 * c, 2 * c))
+        cpa.unpermute(win, cp, seq, row_begin=r * 2 * c, out=back)
+    assert torch.equal(back.cpu(), x)
+    # an odd window and its scatter
+    b0, n = 3, seq // 2 - 1
+    win = cpa.permute(xd, cp, row_begin=b0, row_count=n)
+    assert torch.equal(win.cpu(), oatt.permute_ref(x, seq, cp, b0, n))
+    dst = torch.zeros_like(x)
+    got = cpa.unpermute(win, cp, seq, row_begin=b0, out=torch.zeros_like(xd)).cpu()
+    assert torch.equal(got, oatt.unpermute_ref(oatt.permute_ref(x, seq, cp, b0, n), dst, seq, cp, b0))
+
+
+def test_permute_last_axis_lse_layout():
+    announce("permute along the last axis of [B, H, S] fp32")
+    B, H, S, cp = 2, 6, 256, 4
+    x = torch.randn(B, H, S)
+    xd = x.to(DEV)
+    y = cpa.permute(xd, cp, dim=2).cpu()
+    perm = olb.load_balance_perm(S, cp)
+    assert torch.equal(y, x[:, :, perm])
+    back = cpa.unpermute(y.to(DEV), cp, S, dim=2).cpu()
+    assert torch.equal(back, x)
+
+
+# ----------------------------------------------------------------------------- attention, small full
+
+SMALL = [
+    # name, batch, seq, cps, hq, hkv, dqk, dv, dtype, seed
+    ("tiny-cp2-fp32", 1, 512, (2,), 4, 2, 64, 64, torch.float32, 1),
+    ("gqa-g4-bf16", 1, 1024, (4, 1), 8, 2, 128, 128, torch.bfloat16, 11),
+    ("ragged-c100-bf16", 1, 600, (3,), 6, 3, 128, 128, torch.bfloat16, 12),
+    ("mla-192-128-bf16", 1, 512, (2,), 4, 4, 192, 128, torch.bfloat16, 13),
+    ("d64-g4-bf16", 1, 256, (1, 2), 4, 1, 64, 64, torch.bfloat16, 14),
+    ("batch2-g8-bf16", 2, 384, (2,), 16, 2, 128, 128, torch.bfloat16, 15),
+    ("g16-bf16", 1, 256, (2,), 16, 1, 128, 128, torch.bfloat16, 16),
+    ("fp32-d128", 1, 256, (2,), 2, 2, 128, 128, torch.float32, 17),
+    ("chunk1-bf16", 1, 4, (2, 1), 1, 1, 64, 64, torch.bfloat16, 18),
+    ("chunk1-cp4-fp32", 1, 8, (4,), 2, 1, 64, 64, torch.float32, 19),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_attention_small_all_ranks(case):
+    name, batch, seq, cps, hq, hkv, dqk, dv, dtype, seed = case
+    pf = Prefill(batch, seq, hq, hkv, dqk, dv, dtype, seed)
+    for cp in cps:
+        for r in range(cp):
+            check_rank(pf, cp, r, tag=name)
+
+
+def test_sharded_outputs_reassemble_to_full_causal_attention():
+    """Concatenated, un-permuted per-rank outputs equal un-sharded causal attention (the
+    relation the CP unit test of PR 2023 checks), on the GPU and against the oracle."""
+    announce("reassemble cp=4 ranks vs cp=1 and vs oracle full causal attention")
+    seq, hq, hkv, d, cp = 1024, 8, 2, 128, 4
+    pf = Prefill(1, seq, hq, hkv, d, d, torch.bfloat16, 21)
+    c = seq // (2 * cp)
+    O_nat = torch.zeros((1, seq, hq, d), dtype=torch.bfloat16, device=DEV)
+    L_nat = torch.zeros((1, hq, seq), dtype=torch.float32, device=DEV)
+    for r in range(cp):
+        o, lse = pf.gpu_rank(cp, r)
+        cpa.unpermute(o, cp, seq, row_begin=r * 2 * c, out=O_nat)
+        cpa.unpermute(lse, cp, seq, dim=2, row_begin=r * 2 * c, out=L_nat)
+    o1, l1 = pf.gpu_rank(1, 0)
+    nat = np.arange(seq)
+    O_ref, L_ref = oatt.causal_attention_ref(pf.q, pf.k, pf.v, nat, nat, pf.scale)
+    assert_close(O_nat.float().cpu().numpy(), O_ref, 2e-2, "reassembled O vs oracle")
+    assert_close(L_nat.cpu().numpy(), L_ref, 2e-2, "reassembled LSE vs oracle")
+    assert_close(O_nat.float().cpu().numpy(), o1.float().cpu().numpy(), 2e-2, "reassembled O vs cp=1")
+
+
+def test_explicit_positions_match_implicit_and_unbalanced_shard():
+    announce("q_positions given explicitly; contiguous (unbalanced) shard positions")
+    seq, cp, hq, hkv, d = 512, 2, 4, 2, 128
+    pf = Prefill(1, seq, hq, hkv, d, d, torch.bfloat16, 22)
+    pos = cpa.lb_positions(seq, cp, 256, 256).to(DEV)
+    o_imp, l_imp = pf.gpu_rank(cp, 1)
+    o_exp, l_exp = pf.gpu_rank(cp, 1, q_positions=pos)
+    assert torch.equal(o_imp, o_exp) and torch.equal(l_imp, l_exp)
+    # rows taken contiguously from the natural sequence (no load balance) against permuted K/V
+    kp, vp = pf.kv_perm(cp)
+    for r in range(cp):
+        rows = torch.arange(r * seq // cp, (r + 1) * seq // cp, dtype=torch.int32)
+        qs = pf.qd[:, rows.long().to(DEV)].contiguous()
+        o, lse = cpa.attention_fwd(qs, kp, vp, cp, r, q_positions=rows.to(DEV), scale=pf.scale)
+        O_ref, L_ref = oatt.causal_attention_ref(pf.q[:, rows.long()], oatt.permute_ref(pf.k, seq, cp),
+                                                 oatt.permute_ref(pf.v, seq, cp), rows.numpy(),
+                                                 olb.load_balance_perm(seq, cp), pf.scale)
+        assert_close(o.float().cpu().numpy(), O_ref, 2e-2, f"unbalanced O r={r}")
+        assert_close(lse.cpu().numpy(), L_ref, 2e-2, f"unbalanced LSE r={r}")
+
+
+def test_attention_is_deterministic():
+    announce("determinism: two identical calls")
+    pf = Prefill(1, 2048, 16, 2, 128, 128, torch.bfloat16, 23)
+    a = pf.gpu_rank(2, 1)
+    b = pf.gpu_rank(2, 1)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------- full-size, sampled rows
+
+_FULL = {}
+
+
+def full_workload(w):
+    """One set of full-size inputs at a time (the 131072-token one holds ~3 GB on the host)."""
+    if w.name not in _FULL:
+        _FULL.clear()
+        torch.cuda.empty_cache()
+        announce(f"generating {w.name}")
+        _FULL[w.name] = Prefill(w.batch, w.seq, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype, w.seed)
+    return _FULL[w.name]
+
+
+FULL_CASES = [(w, cp, r) for w in (synth.LLAMA2_7B_S8K, synth.DEEPSEEK_V3_MLA_S32K, synth.LLAMA31_70B_S131K)
+              for cp in w.cps for r in range(cp)]
+
+
+@pytest.mark.parametrize("w,cp,rank", FULL_CASES, ids=[f"{w.name}-cp{cp}-r{r}" for w, cp, r in FULL_CASES])
+def test_attention_full_size_sampled(w, cp, rank):
+    pf = full_workload(w)
+    c = w.seq // (2 * cp)
+    rows = sample_rows(c, 16 if w.seq >= 100000 else 24, seed=1000 * cp + rank)
+    check_rank(pf, cp, rank, rows=rows, tag=w.name)
+
+
+def test_permute_full_size_llama70b():
+    """Full-size gather/scatter of the 131072-token workload (runs after its attention tests so
+    the cached inputs are reused)."""
+    w = synth.LLAMA31_70B_S131K
+    pf = full_workload(w)
+    announce(f"permute {w.name}: K full, Q rank-3 window and its scatter")
+    assert torch.equal(cpa.permute(pf.kd, 8).cpu(), oatt.permute_ref(pf.k, w.seq, 8))
+    c = w.seq // 16
+    win = cpa.permute(pf.qd, 8, row_begin=3 * 2 * c, row_count=2 * c)
+    assert torch.equal(win.cpu(), oatt.permute_ref(pf.q, w.seq, 8, 3 * 2 * c, 2 * c))
+    out = torch.zeros_like(pf.qd)
+    cpa.unpermute(win, 8, w.seq, row_begin=3 * 2 * c, out=out)
+    pos = torch.from_numpy(olb.shard_positions(w.seq, 8, 3))
+    assert torch.equal(out[:, pos.to(DEV)].cpu(), pf.q[:, pos])
+
+
+def test_tiny_workload_full():
+    w = synth.TINY_CP2_F32
+    pf = Prefill(w.batch, w.seq, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype, w.seed)
+    for r in range(2):
+        check_rank(pf, 2, r, tag=w.name)
+
+
+# ----------------------------------------------------------------------------- decode
+
+def run_decode(lengths, q, kc, vc, scale):
+    o, lse = cpa.decode(q.to(DEV), kc.to(DEV), vc.to(DEV), lengths.to(DEV), scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def test_decode_full_workload_with_poisoned_tail():
+    w = synth.MIXTRAL_8X22B_DECODE
+    announce(f"decode {w.name} (NaN beyond each length)")
+    lengths, q, kc, vc = synth.workload_decode_inputs(w)
+    O_ref, L_ref = oatt.decode_ref(q, kc, vc, lengths.numpy(), w.scale)
+    for b in range(w.batch):
+        kc[b, :, lengths[b]:] = float("nan")
+        vc[b, :, lengths[b]:] = float("nan")
+    o, lse = run_decode(lengths, q, kc, vc, w.scale)
+    assert_close(o, O_ref, 2e-2, "decode O")
+    assert_close(lse, L_ref, 2e-2, "decode LSE")
+
+
+@pytest.mark.parametrize("batch,hq,hkv,d,max_len,dtype,lens", [
+    (4, 48, 8, 128, 2048, torch.bfloat16, [1, 2048, 256, 257]),
+    (3, 16, 1, 128, 300, torch.bfloat16, [300, 1, 255]),     # G=16 > heads per pass
+    (2, 8, 8, 64, 513, torch.float32, [513, 17]),
+    (5, 12, 4, 64, 1000, torch.bfloat16, [999, 1000, 512, 3, 768]),
+    (2, 4, 2, 128, 64, torch.float32, [64, 33]),
+])
+def test_decode_edge_lengths(batch, hq, hkv, d, max_len, dtype, lens):
+    announce(f"decode B={batch} Hq={hq} Hkv={hkv} D={d} Lmax={max_len} {dtype} lens={lens}")
+    lengths, q, kc, vc = synth.decode_inputs(batch, hq, hkv, d, max_len, 1, max_len, dtype, seed=batch + d)
+    lengths = torch.tensor(lens, dtype=torch.int32)
+    scale = 1.0 / math.sqrt(d)
+    O_ref, L_ref = oatt.decode_ref(q, kc, vc, lengths.numpy(), scale)
+    for b in range(batch):
+        kc[b, :, lens[b]:] = float("nan")
+        vc[b, :, lens[b]:] = float("nan")
+    o, lse = run_decode(lengths, q, kc, vc, scale)
+    tol = TOL[dtype]
+    assert_close(o, O_ref, tol, "decode O")
+    assert_close(lse, L_ref, tol, "decode LSE")

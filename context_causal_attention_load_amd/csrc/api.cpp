@@ -190,8 +190,7 @@ int cp_attention_fwd(const void* q_shard, const void* k, const void* v, const in
 }
 
 size_t gqa_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t max_len, int32_t d) {
-  (void)hkv;
-  if (batch <= 0 || hq <= 0 || max_len <= 0 || d <= 0) return 0;
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || max_len <= 0 || d <= 0) return 0;
   return (size_t)batch * hq * decode_nsplit(max_len) * (size_t)(d + 2) * sizeof(float);
 }
 

@@ -60,14 +60,16 @@ struct DecodeArgs {
   const int32_t* lengths;
   void* o;
   float* lse;
-  float* ws;
+  float* ws;  // split partials [B, Hq, nsplit, d + 2]
   int batch, hq, hkv, d, max_len, nsplit, split_len;
   float scale;
 };
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 
-// Decode split geometry shared by the workspace-size query and the launcher.
+// Decode split geometry, shared by the workspace-size query and the launcher. The workspace
+// holds the split partials [batch, hq, nsplit, d + 2] in float32: d unnormalised outputs, then
+// the split's max and sum (log2 units).
 constexpr int kDecodeSplitLen = 256;
 inline int decode_nsplit(int max_len) { return (max_len + kDecodeSplitLen - 1) / kDecodeSplitLen; }
 

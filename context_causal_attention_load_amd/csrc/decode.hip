@@ -10,9 +10,14 @@
 //  * Split-K: workgroup (split s, kv head g, sequence b) owns keys [s*L_s, (s+1)*L_s) clipped
 //    to len_b and all G query heads of g; it writes (max, sum, unnormalised output) partials.
 //    Splits past len_b exit at once, so nothing beyond the valid length is ever loaded.
-//  * A second kernel merges the partials of each (b, h) with log-sum-exp weights.
-//  * Loads are 16 bytes per lane and a key row is spread over D*elt/16 lanes, so each
-//    wavefront load instruction reads whole contiguous rows of the (b, g) cache slab.
+//  * Second pass: the partials of each (b, h) are merged with log-sum-exp weights.
+//  * bf16, D = 128, G <= 8 (the fast path): every K and V load of the split is issued before any
+//    arithmetic, so a workgroup keeps its whole 2 x 64 KB split in flight; scores use v_dot2
+//    on bf16 pairs with 4 lanes per key row and a DPP reduction.
+//  * Other cases (fp32 caches, D = 64, G > 8) use a simpler split kernel with the same partial layout.
+//  * The merge is a separate launch: merging inside the split kernel (last workgroup to
+//    arrive) needs a device-scope release per workgroup, which on this part writes back the
+//    whole L2 and costs far more than the second launch.
 #include "common.h"
 
 namespace cpattn {
@@ -201,6 +206,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   }
 }
 
+// Second pass: thread d of block (b, h) merges every split's partial of that (b, h). All of a
+// thread's partial loads are issued before the arithmetic (up to kMergeUnroll splits).
+constexpr int kMergeUnroll = 16;
+
 template <typename T, int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
   const int bh = blockIdx.x;
@@ -210,17 +219,255 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
   len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
   const int nvalid = (len + p.split_len - 1) / p.split_len;
   const float* part = p.ws + (int64_t)bh * p.nsplit * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < nvalid; ++s) {
-    const float w = __builtin_amdgcn_exp2f(part[s * (D + 2) + D] - M);
-    L = __builtin_fmaf(w, part[s * (D + 2) + D + 1], L);
-    acc = __builtin_fmaf(w, part[s * (D + 2) + d], acc);
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  if (nvalid <= kMergeUnroll) {
+    float m[kMergeUnroll], l[kMergeUnroll], o[kMergeUnroll];
+#pragma unroll
+    for (int s = 0; s < kMergeUnroll; ++s) {
+      if (s < nvalid) {
+        m[s] = part[s * (D + 2) + D];
+        l[s] = part[s * (D + 2) + D + 1];
+        o[s] = part[s * (D + 2) + d];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kMergeUnroll; ++s)
+      if (s < nvalid) M = fmaxf(M, m[s]);
+#pragma unroll
+    for (int s = 0; s < kMergeUnroll; ++s) {
+      if (s < nvalid) {
+        const float w = __builtin_amdgcn_exp2f(m[s] - M);
+        L = __builtin_fmaf(w, l[s], L);
+        acc = __builtin_fmaf(w, o[s], acc);
+      }
+    }
+  } else {
+    for (int s = 0; s < nvalid; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
+    for (int s = 0; s < nvalid; ++s) {
+      const float w = __builtin_amdgcn_exp2f(part[s * (D + 2) + D] - M);
+      L = __builtin_fmaf(w, part[s * (D + 2) + D + 1], L);
+      acc = __builtin_fmaf(w, part[s * (D + 2) + d], acc);
+    }
   }
-  T* o = static_cast<T*>(p.o) + (int64_t)bh * D;
-  o[d] = (T)(acc / L);
+  T* out = static_cast<T*>(p.o) + (int64_t)bh * D;
+  out[d] = (T)(acc / L);
   if (p.lse && d == 0) p.lse[bh] = (M + __builtin_amdgcn_logf(L)) * kLn2;
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16 fast path: one workgroup of 512 threads per (split of 256 keys, kv head, sequence)
+// ------------------------------------------------------------------------------------------
+constexpr int kFastThreads = 512;
+constexpr int kFastWaves = kFastThreads / 64;
+
+// Reinterpret one 32-bit word as a bf16 pair. The word is taken as a scalar argument: applying
+// __builtin_bit_cast to an ext-vector element directly (v[i], v.y) makes this clang read
+// element 0 whatever the index.
+__device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) { return __builtin_bit_cast(bf16x2, u); }
+
+__device__ __forceinline__ float dot8_bf16(const u32x4& a, const u32x4& b, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned ai = a[i], bi = b[i];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ai), as_bf16x2(bi), acc, false);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float dpp_quad_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+template <int D, int G>
+__global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecParams p) {
+  constexpr int SL = kDecodeSplitLen;
+  constexpr int KC = D / 32;              // 16-byte K chunks per lane (4 lanes per key row)
+  constexpr int KROWS = kFastThreads / 4;  // key rows per K pass
+  constexpr int KP = SL / KROWS;           // K passes
+  constexpr int LPRV = D / 8;              // lanes per V row (one 16-byte chunk each)
+  constexpr int VS = kFastThreads / LPRV;  // V row slots
+  constexpr int VR = SL / VS;              // V rows per lane (consecutive pairs share a v_dot2)
+  static_assert(SL % KROWS == 0 && SL % VS == 0 && VR % 2 == 0, "split / thread layout mismatch");
+
+  __shared__ float s_s[G][SL];                                   // scores, log2 units
+  __shared__ __attribute__((aligned(16))) __bf16 s_pb[G][VS][VR];  // bf16 probabilities by V slot
+  __shared__ __attribute__((aligned(16))) __bf16 s_q[G][D];
+  __shared__ float s_red[kFastWaves][G][D];
+  __shared__ float s_m[G], s_l[G];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int len = p.lengths[b];
+  len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+  const int k0 = split * SL;
+  if (k0 >= len) return;
+  const int nk = min(SL, len - k0);
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+
+  const int64_t slab = ((int64_t)b * p.Hkv + g) * p.max_len * D;
+  const __bf16* kb = static_cast<const __bf16*>(p.k) + slab + (int64_t)k0 * D;
+  const __bf16* vb = static_cast<const __bf16*>(p.v) + slab + (int64_t)k0 * D;
+
+  // ---- issue every K and V load of the split up front. K: a lane quad owns a key row and
+  // each load instruction of the quad reads one contiguous 64-byte segment of it.
+  const int kq = tid % 4;
+  u32x4 kr[KP][KC];
+#pragma unroll
+  for (int ps = 0; ps < KP; ++ps) {
+    const int row = ps * KROWS + tid / 4;
+#pragma unroll
+    for (int cc = 0; cc < KC; ++cc) {
+      kr[ps][cc] = row < nk ? *reinterpret_cast<const u32x4*>(kb + (int64_t)row * D + (cc * 4 + kq) * 8)
+                            : u32x4{0, 0, 0, 0};
+    }
+  }
+  const int vc = tid % LPRV;
+  const int vslot = tid / LPRV;
+  u32x4 vr[VR];
+#pragma unroll
+  for (int i = 0; i < VR; ++i) {
+    const int row = i * VS + vslot;
+    vr[i] = row < nk ? *reinterpret_cast<const u32x4*>(vb + (int64_t)row * D + vc * 8) : u32x4{0, 0, 0, 0};
+  }
+
+  // ---- the group's query vectors into LDS
+  const __bf16* qg = static_cast<const __bf16*>(p.q) + ((int64_t)b * p.Hq + (int64_t)g * p.G) * D;
+  for (int idx = tid; idx < G * (D / 8); idx += kFastThreads) {
+    const int h = idx / (D / 8), c = idx % (D / 8);
+    *reinterpret_cast<u32x4*>(&s_q[h][c * 8]) = *reinterpret_cast<const u32x4*>(qg + (int64_t)h * D + c * 8);
+  }
+  __syncthreads();
+
+  // ---- scores (log2 units): 4 lanes per key row, DPP sum inside each lane quad
+#pragma unroll
+  for (int ps = 0; ps < KP; ++ps) {
+    const int row = ps * KROWS + tid / 4;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      {
+        float acc = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < KC; ++cc)
+          acc = dot8_bf16(kr[ps][cc], *reinterpret_cast<const u32x4*>(&s_q[h][(cc * 4 + kq) * 8]), acc);
+        acc += dpp_quad_xor1(acc);
+        acc += dpp_quad_xor2(acc);
+        if (kq == 0) s_s[h][row] = row < nk ? acc * p.scale_log2 : -INFINITY;
+        // keep the scheduler from hoisting every head's query reads (register pressure)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- per-head max / probabilities / sum over the split: one wave per head. Probabilities
+  // are rounded to bf16 once; the sum adds the rounded values, and they are stored where the
+  // P V step reads them (by V row slot, consecutive rows of a slot adjacent).
+  if (wave < G) {
+    float x[SL / 64];
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < SL / 64; ++j) {
+      x[j] = s_s[wave][lane + 64 * j];
+      m = fmaxf(m, x[j]);
+    }
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float l = 0.f;
+#pragma unroll
+    for (int j = 0; j < SL / 64; ++j) {
+      const int row = lane + 64 * j;
+      const __bf16 e = (__bf16)__builtin_amdgcn_exp2f(x[j] - m);
+      s_pb[wave][row % VS][row / VS] = e;
+      l += (float)e;
+    }
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+    if (lane == 0) {
+      s_m[wave] = m;
+      s_l[wave] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- unnormalised P V: v_dot2 over pairs of this lane's rows (p pair . v pair per dim).
+  // The (row a, row b) bf16 pairs of every dim are formed once; heads are then done one at a
+  // time so only 8 accumulators are live.
+  static_assert(LPRV == 16, "the slot reduction below assumes 16 lanes per V row");
+  unsigned vp[VR / 2][8];
+#pragma unroll
+  for (int pi = 0; pi < VR / 2; ++pi) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned a = vr[2 * pi][j], c = vr[2 * pi + 1][j];
+      vp[pi][2 * j] = __builtin_amdgcn_perm(c, a, 0x05040100u);      // dim 2j of rows (a, b)
+      vp[pi][2 * j + 1] = __builtin_amdgcn_perm(c, a, 0x07060302u);  // dim 2j+1 of rows (a, b)
+    }
+  }
+  // Sum over the 4 row slots of the wave with lane-swap "transpose" steps, each reducing two
+  // accumulators: after the 32-lane step the lower half of register i holds dim 2i and the upper
+  // half dim 2i+1; after the 16-lane step each 16-lane row of register j holds one of dims
+  // 4j..4j+3 (rows 0..3 -> 4j, 4j+2, 4j+1, 4j+3).
+  const int rowq = lane / 16;
+  const int tsel = (rowq == 0) ? 0 : (rowq == 1 ? 2 : (rowq == 2 ? 1 : 3));
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float a8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a8[e] = 0.f;
+#pragma unroll
+    for (int pi = 0; pi < VR / 2; ++pi) {
+      const unsigned pw = reinterpret_cast<const unsigned*>(&s_pb[h][vslot][0])[pi];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a8[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw), as_bf16x2(vp[pi][e]), a8[e], false);
+    }
+    float hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(a8[2 * i]), __float_as_uint(a8[2 * i + 1]), false,
+                                                 false);
+      hv[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(hv[2 * j]), __float_as_uint(hv[2 * j + 1]), false,
+                                                 false);
+      s_red[wave][h][vc * 8 + 4 * j + tsel] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    }
+  }
+  __syncthreads();
+
+  // ---- this split's partial: (o[0..D), max, sum) per head
+  for (int idx = tid; idx < G * D; idx += kFastThreads) {
+    const int h = idx / D, d = idx % D;
+    float x = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kFastWaves; ++wv) x += s_red[wv][h][d];
+    float* part = p.ws + (((int64_t)b * p.Hq + g * p.G + h) * p.nsplit + split) * (D + 2);
+    part[d] = x;
+    if (d == 0) {
+      part[D] = s_m[h];
+      part[D + 1] = s_l[h];
+    }
+  }
+}
+
+template <int D, int G>
+void launch_fast(const DecParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_bf16_split_kernel<D, G>), dim3(p.nsplit, p.Hkv, p.B), dim3(kFastThreads), 0, stream,
+                     p);
+}
+
+bool launch_fast_128(const DecParams& p, hipStream_t stream) {
+  switch (p.G) {
+    case 1: launch_fast<128, 1>(p, stream); return true;
+    case 2: launch_fast<128, 2>(p, stream); return true;
+    case 3: launch_fast<128, 3>(p, stream); return true;
+    case 4: launch_fast<128, 4>(p, stream); return true;
+    case 5: launch_fast<128, 5>(p, stream); return true;
+    case 6: launch_fast<128, 6>(p, stream); return true;
+    case 7: launch_fast<128, 7>(p, stream); return true;
+    case 8: launch_fast<128, 8>(p, stream); return true;
+    default: return false;
+  }
 }
 
 template <typename T>
@@ -242,6 +489,12 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   p.split_len = a.split_len;
   p.scale_log2 = a.scale * kLog2e;
   if (p.B == 0 || p.Hq == 0) return hipSuccess;
+  if constexpr (sizeof(T) == 2) {
+    if (a.d == 128 && launch_fast_128(p, stream)) {
+      hipLaunchKernelGGL((decode_merge_kernel<T, 128>), dim3(p.B * p.Hq), dim3(128), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   dim3 g1(p.nsplit, p.Hkv, p.B);
   if (a.d == 128) {
     hipLaunchKernelGGL((decode_split_kernel<T, 128>), g1, dim3(kThreads), 0, stream, p);

@@ -143,7 +143,8 @@ int cp_attention_fwd(const void* q_shard, const void* k, const void* v,
  *   o        [B, Hq, D] same dtype as q (output)
  *   lse      [B, Hq] float32 (output, may be NULL)
  *   workspace, workspace_bytes: device scratch of at least gqa_decode_workspace_bytes(...)
- *            bytes, owned by the caller; its contents on entry do not matter.
+ *            bytes, owned by the caller, holding the split partials between the two passes.
+ *            Its contents on entry do not matter. Calls sharing one workspace must not overlap.
  * Supported: bf16 and f32 with D in {64, 128}. CPA_EINVAL for hq % hkv != 0, null or misaligned
  * pointers, a workspace that is too small, or a non-positive scale. */
 size_t gqa_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t max_len, int32_t d);

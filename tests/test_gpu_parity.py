@@ -316,3 +316,17 @@ def test_decode_edge_lengths(batch, hq, hkv, d, max_len, dtype, lens):
     tol = TOL[dtype]
     assert_close(o, O_ref, tol, "decode O")
     assert_close(lse, L_ref, tol, "decode LSE")
+
+
+def test_decode_workspace_reuse():
+    """One workspace (garbage-filled) serves repeated calls and a smaller batch afterwards."""
+    announce("decode workspace reuse")
+    B, hq, hkv, d, lmax = 6, 12, 2, 128, 700
+    ws = torch.full((cpa.decode_workspace_bytes(B, hq, hkv, lmax, d),), 0x7F, dtype=torch.uint8, device=DEV)
+    for it, (b, seed) in enumerate([(6, 31), (6, 32), (3, 33)]):
+        lengths, q, kc, vc = synth.decode_inputs(b, hq, hkv, d, lmax, 1, lmax, torch.bfloat16, seed=seed)
+        o, lse = cpa.decode(q.to(DEV), kc.to(DEV), vc.to(DEV), lengths.to(DEV), workspace=ws)
+        torch.cuda.synchronize()
+        O_ref, L_ref = oatt.decode_ref(q, kc, vc, lengths.numpy(), 1.0 / math.sqrt(d))
+        assert_close(o.float().cpu().numpy(), O_ref, 2e-2, f"decode O call {it}")
+        assert_close(lse.cpu().numpy(), L_ref, 2e-2, f"decode LSE call {it}")

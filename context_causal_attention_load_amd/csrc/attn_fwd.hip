@@ -25,8 +25,11 @@
 //    order, chunk i sitting at permuted offset lb_chunk_offset(i). Only keys with position
 //    <= the workgroup's largest query position are visited; tiles whose last key position is
 //    <= its smallest query position skip the mask.
-//  * Global->LDS staging is double-buffered through registers: the loads for tile t+1 are in
-//    flight while tile t is computed. LDS rows use an XOR swizzle of 16-byte chunks.
+//  * K/V tiles are double-buffered in LDS and filled with direct global->LDS copies
+//    (global_load_lds_dwordx4): the copy of tile t+1 is in flight while tile t is computed and
+//    uses no registers. LDS rows use an XOR swizzle of 16-byte chunks that keeps both the
+//    K-fragment reads and the transposing V reads free of bank conflicts.
+//  * Scheduling groups keep every LDS fragment read two MFMAs ahead of its use.
 //  * Workgroup order is XCD-aware and heavy-first: consecutive work items (same KV head,
 //    neighbouring row blocks) go to the same XCD so they share its L2, and row blocks with the
 //    latest positions (most keys) start first.
@@ -55,14 +58,12 @@ struct FwdParams {
   float scale_log2;
 };
 
-// 16-byte-chunk XOR swizzle of an LDS tile row; stays inside aligned groups of 16 (or 8)
-// chunks so it never leaves the row.
 template <int CH>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (CH % 16 == 0) {
-    return ((row & 7) << 1) | ((row >> 3) & 1);
+    return ((row & 3) << 2) | ((row >> 2) & 3);
   } else {
-    return ((row & 3) << 1) | ((row >> 2) & 1);
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
   }
 }
 
@@ -84,6 +85,16 @@ __device__ __forceinline__ int wave_min_i(int x) {
 __device__ __forceinline__ int wave_max_i(int x) {
   for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off));
   return x;
+}
+
+
+// 16-byte global -> LDS copy per lane (gfx950 global_load_lds_dwordx4): lane l's bytes land at
+// LDS address lds_wave_base + 16*l. Issued through inline asm so that the compiler does not
+// make the reads of the other LDS stage wait for it; the caller waits (vmcnt) before the barrier
+// that publishes the stage.
+__device__ __forceinline__ void dma16(const void* gptr, const char* lds_wave_base) {
+  const unsigned lds_addr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
 }
 
 struct WorkItem {
@@ -202,6 +213,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
         qg + (((int64_t)w.b * p.Sq + row) * p.Hq + head) * DQK);
 #pragma unroll
     for (int ks = 0; ks < C::QK_STEPS; ++ks) qf[ks] = qrow[2 * ks + hl];
+    // make the compiler wait for the Q loads here: otherwise its wait counting inside the loop
+    // would also wait for the tile DMAs issued through inline asm
+#pragma unroll
+    for (int ks = 0; ks < C::QK_STEPS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
   const int64_t kv_row_elems_k = (int64_t)p.Hkv * DQK;
@@ -212,48 +227,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   const int c = p.c;
   const int imax = min(qmax / c, 2 * p.cp - 1);
 
-  // staging registers for the next tile
-  u32x4 kst[C::K_LOADS];
-  u32x4 vst[C::V_LOADS];
-
-  auto load_tile = [&](const TileCursor& tc) {
+  // DMA slots: wave-instruction (u, wave) fills LDS bytes [1024*(u*kWaves + wave), +1024) of a
+  // tile, lane l at +16*l; the lane loads whichever (row, chunk) the swizzle puts there.
+  constexpr int K_DMA = C::K_LOADS, V_DMA = C::V_LOADS;
+  int k_slot[K_DMA], v_slot[V_DMA];  // (row << 16) | element offset
+#pragma unroll
+  for (int u = 0; u < K_DMA; ++u) {
+    const int pos = (u * kWaves + wave) * 1024 + lane * 16;
+    const int row = pos / (C::KCH * 16), phys = (pos % (C::KCH * 16)) / 16;
+    k_slot[u] = (row << 16) | ((phys ^ swz<C::KCH>(row)) * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < V_DMA; ++u) {
+    const int pos = (u * kWaves + wave) * 1024 + lane * 16;
+    const int row = pos / (C::VCH * 16), phys = (pos % (C::VCH * 16)) / 16;
+    v_slot[u] = (row << 16) | ((phys ^ swz<C::VCH>(row)) * 8);
+  }
+  auto dma_tile = [&](const TileCursor& tc, int b) {
     const int64_t prow0 = lb_chunk_offset(tc.chunk, c, p.cp) + tc.t0;
-    const int nvalid = min(kBK, c - tc.t0);
+    const int last = min(kBK, c - tc.t0) - 1;
+    const __bf16* kt = kbase + prow0 * kv_row_elems_k;
+    const __bf16* vt = vbase + prow0 * kv_row_elems_v;
+    char* kl = lds + b * C::STAGE;
+    char* vl = kl + C::K_BYTES;
 #pragma unroll
-    for (int u = 0; u < C::K_LOADS; ++u) {
-      int id = tid + u * kThreads;
-      int row = id / C::KCH, ch = id % C::KCH;
-      if (row < nvalid) {
-        kst[u] = *reinterpret_cast<const u32x4*>(kbase + (prow0 + row) * kv_row_elems_k + ch * 8);
-      } else {
-        kst[u] = u32x4{0, 0, 0, 0};
-      }
+    for (int u = 0; u < K_DMA; ++u) {
+      const __bf16* src = kt + (int64_t)min(k_slot[u] >> 16, last) * kv_row_elems_k + (k_slot[u] & 0xffff);
+      dma16(src, kl + (u * kWaves + wave) * 1024);
     }
 #pragma unroll
-    for (int u = 0; u < C::V_LOADS; ++u) {
-      int id = tid + u * kThreads;
-      int row = id / C::VCH, ch = id % C::VCH;
-      if (row < nvalid) {
-        vst[u] = *reinterpret_cast<const u32x4*>(vbase + (prow0 + row) * kv_row_elems_v + ch * 8);
-      } else {
-        vst[u] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* kb = lds + buf * C::STAGE;
-    char* vb = kb + C::K_BYTES;
-#pragma unroll
-    for (int u = 0; u < C::K_LOADS; ++u) {
-      int id = tid + u * kThreads;
-      int row = id / C::KCH, ch = id % C::KCH;
-      *reinterpret_cast<u32x4*>(kb + row * (C::KCH * 16) + ((ch ^ swz<C::KCH>(row)) * 16)) = kst[u];
-    }
-#pragma unroll
-    for (int u = 0; u < C::V_LOADS; ++u) {
-      int id = tid + u * kThreads;
-      int row = id / C::VCH, ch = id % C::VCH;
-      *reinterpret_cast<u32x4*>(vb + row * (C::VCH * 16) + ((ch ^ swz<C::VCH>(row)) * 16)) = vst[u];
+    for (int u = 0; u < V_DMA; ++u) {
+      const __bf16* src = vt + (int64_t)min(v_slot[u] >> 16, last) * kv_row_elems_v + (v_slot[u] & 0xffff);
+      dma16(src, vl + (u * kWaves + wave) * 1024);
     }
   };
 
@@ -267,8 +272,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   TileCursor tc{0, 0};
-  load_tile(tc);
-  store_tile(0);
+  dma_tile(tc, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int buf = 0;
 
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     TileCursor nx = tc;
     next_tile(nx, c, qmax);
     const bool has_next = nx.chunk <= imax;
-    if (has_next) load_tile(nx);
+    if (has_next) dma_tile(nx, buf ^ 1);  // that stage was last read in the previous iteration
 
     const char* kb = lds + buf * C::STAGE;
     const char* vb = kb + C::K_BYTES;
@@ -303,6 +308,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
       }
       s[mb] = acc;
     }
+    // keep each K-fragment read two MFMAs ahead of its use
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * C::QK_STEPS - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
     // ---- mask (only tiles that reach past the smallest query position, or partial tiles)
     const int kpos0 = tc.chunk * c + tc.t0;
@@ -376,8 +389,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
         oacc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[mv], 0, 0, 0);
       }
     }
+    // same for the transposed V reads (two per MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * C::MV - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
-    if (has_next) store_tile(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     buf ^= 1;
     tc = nx;

@@ -36,6 +36,23 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
+def profiled_traffic(profile, source):
+    """HBM bytes per launch recorded in a committed rocprofv3 summary under profiles/ (FETCH_SIZE
+    and WRITE_SIZE, scaled by a plain-copy calibration), or None when the summary is missing or
+    the kernel source has changed since the counters were taken (its sha256 differs)."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, "profiles", profile)).read()
+        src = open(os.path.join(ROOT, "context_causal_attention_load_amd", "csrc", source), "rb").read()
+    except OSError:
+        return None
+    fields = dict(line.split(" = ", 1) for line in text.splitlines()
+                  if line.startswith(("traffic_bytes_per_launch = ", "kernel_source_sha256 = ")))
+    if fields.get("kernel_source_sha256", "").strip() != hashlib.sha256(src).hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def useful_flops(seq, cp, hq, dqk, dv, batch=1):
     # every rank of a balanced split sees exactly c*(S+1) causal (query, key) pairs
     c = seq // (2 * cp)
@@ -201,7 +218,9 @@ def main():
                    "head_dim_v": w.d_v, "parallelism": "one context-parallel rank (cp=8) per GPU",
                    "ranks_timed": sorted(pre["per_rank_ms"].keys())},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": profiled_traffic("attn_fwd_bf16_llama70b_s131072_cp8.md", "attn_fwd.hip"),
+                     "traffic_unit": "HBM bytes per launch",
                      "kernel": "attn_fwd_bf16_kernel<128,128>", "kernel_avg_ms": round(attn_avg_ms, 4),
                      "useful_flop_per_launch": pre["flops"]},
         "per_rank_step_ms": {str(r): round(t, 3) for r, t in pre["per_rank_ms"].items()},
@@ -213,7 +232,10 @@ def main():
                             "median_us": round(d["median_ms"] * 1e3, 2), "min_us": round(d["min_ms"] * 1e3, 2),
                             "roofline": {"bound": "hbm", "achieved": round(d["gbs"], 1), "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": round(d["gbs"] / PEAK_HBM_GBS, 4),
-                                         "traffic": None, "algorithmic_bytes": d["bytes"]}}
+                                         "traffic": profiled_traffic("decode_gqa_mixtral8x22b_b24_l2048.md",
+                                                                     "decode.hip"),
+                                         "traffic_unit": "HBM bytes per call (split + merge)",
+                                         "algorithmic_bytes": d["bytes"]}}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, cp, 0, args.cpu_rows)
         cb.pop("seconds")

@@ -97,6 +97,20 @@ __device__ __forceinline__ void dma16(const void* gptr, const char* lds_wave_bas
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
 }
 
+// The same copy from a wave-uniform base plus a per-lane 32-bit byte offset (the base lives in
+// scalar registers, so a tile's copies need no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void dma16_sv(const char* base, unsigned voff, unsigned lds_wave_addr) {
+  // readfirstlane yields int: both halves go through unsigned so that the low word is
+  // zero-extended (a sign-extended low word would corrupt the high word of the address)
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
+  const char* sbase = reinterpret_cast<const char*>((hi << 32) | lo);
+  const unsigned lds_addr = __builtin_amdgcn_readfirstlane(lds_wave_addr);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 struct WorkItem {
   int b, g, head0, row_blk;
 };
@@ -192,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   WorkItem w;
   if (!decode_item(p, w)) return;
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64;
   const int hl = lane / 32;  // which half of the wave
   const int head = w.head0 + wave / p.wpr;
@@ -202,73 +216,94 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   if (qmax < 0) return;  // no valid row (cannot happen for a non-empty block)
 
   const __bf16* qg = static_cast<const __bf16*>(p.q);
-  const __bf16* kg = static_cast<const __bf16*>(p.k);
-  const __bf16* vg = static_cast<const __bf16*>(p.v);
+  const char* kg = static_cast<const char*>(p.k);
+  const char* vg = static_cast<const char*>(p.v);
+  const float sl2 = p.scale_log2;
 
-  // Q fragment (B operand of S^T = K Q^T): lane holds row (lane&31), dims 16ks + 8hl .. +7
+  // Q fragment (B operand of S^T = K Q^T): lane holds row (lane&31), dims 16ks + 8hl .. +7. The
+  // softmax scale (times log2 e) is folded into Q once, in fp32, before the rounding to bf16,
+  // so the products come out as log2-unit logits.
   bf16x8 qf[C::QK_STEPS];
   {
     int row = my_row < p.Sq ? my_row : p.Sq - 1;
     const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
         qg + (((int64_t)w.b * p.Sq + row) * p.Hq + head) * DQK);
 #pragma unroll
-    for (int ks = 0; ks < C::QK_STEPS; ++ks) qf[ks] = qrow[2 * ks + hl];
+    for (int ks = 0; ks < C::QK_STEPS; ++ks) {
+      const bf16x8 raw = qrow[2 * ks + hl];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * sl2);
+    }
     // make the compiler wait for the Q loads here: otherwise its wait counting inside the loop
     // would also wait for the tile DMAs issued through inline asm
 #pragma unroll
     for (int ks = 0; ks < C::QK_STEPS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
-  const int64_t kv_row_elems_k = (int64_t)p.Hkv * DQK;
-  const int64_t kv_row_elems_v = (int64_t)p.Hkv * DV;
-  const __bf16* kbase = kg + (int64_t)w.b * p.S * kv_row_elems_k + (int64_t)w.g * DQK;
-  const __bf16* vbase = vg + (int64_t)w.b * p.S * kv_row_elems_v + (int64_t)w.g * DV;
+  const int64_t kv_row_bytes_k = (int64_t)p.Hkv * DQK * 2;
+  const int64_t kv_row_bytes_v = (int64_t)p.Hkv * DV * 2;
+  const char* kbase = kg + (int64_t)w.b * p.S * kv_row_bytes_k + (int64_t)w.g * DQK * 2;
+  const char* vbase = vg + (int64_t)w.b * p.S * kv_row_bytes_v + (int64_t)w.g * DV * 2;
 
   const int c = p.c;
   const int imax = min(qmax / c, 2 * p.cp - 1);
 
   // DMA slots: wave-instruction (u, wave) fills LDS bytes [1024*(u*kWaves + wave), +1024) of a
-  // tile, lane l at +16*l; the lane loads whichever (row, chunk) the swizzle puts there.
+  // tile, lane l at +16*l; the lane loads whichever (row, chunk) the swizzle puts there. For a
+  // full tile the source byte offsets from the tile's first row are fixed per lane.
   constexpr int K_DMA = C::K_LOADS, V_DMA = C::V_LOADS;
-  int k_slot[K_DMA], v_slot[V_DMA];  // (row << 16) | element offset
+  int k_row[K_DMA], v_row[V_DMA];
+  unsigned k_col[K_DMA], v_col[V_DMA], k_off[K_DMA], v_off[V_DMA];
 #pragma unroll
   for (int u = 0; u < K_DMA; ++u) {
     const int pos = (u * kWaves + wave) * 1024 + lane * 16;
     const int row = pos / (C::KCH * 16), phys = (pos % (C::KCH * 16)) / 16;
-    k_slot[u] = (row << 16) | ((phys ^ swz<C::KCH>(row)) * 8);
+    k_row[u] = row;
+    k_col[u] = (unsigned)((phys ^ swz<C::KCH>(row)) * 16);
+    k_off[u] = (unsigned)(row * kv_row_bytes_k) + k_col[u];
   }
 #pragma unroll
   for (int u = 0; u < V_DMA; ++u) {
     const int pos = (u * kWaves + wave) * 1024 + lane * 16;
     const int row = pos / (C::VCH * 16), phys = (pos % (C::VCH * 16)) / 16;
-    v_slot[u] = (row << 16) | ((phys ^ swz<C::VCH>(row)) * 8);
+    v_row[u] = row;
+    v_col[u] = (unsigned)((phys ^ swz<C::VCH>(row)) * 16);
+    v_off[u] = (unsigned)(row * kv_row_bytes_v) + v_col[u];
   }
+  const unsigned lds0 = (unsigned)(uintptr_t)lds;
   auto dma_tile = [&](const TileCursor& tc, int b) {
     const int64_t prow0 = lb_chunk_offset(tc.chunk, c, p.cp) + tc.t0;
     const int last = min(kBK, c - tc.t0) - 1;
-    const __bf16* kt = kbase + prow0 * kv_row_elems_k;
-    const __bf16* vt = vbase + prow0 * kv_row_elems_v;
-    char* kl = lds + b * C::STAGE;
-    char* vl = kl + C::K_BYTES;
+    const char* kt = kbase + prow0 * kv_row_bytes_k;
+    const char* vt = vbase + prow0 * kv_row_bytes_v;
+    const unsigned kl = lds0 + b * C::STAGE;
+    const unsigned vl = kl + C::K_BYTES;
+    if (last == kBK - 1) {
 #pragma unroll
-    for (int u = 0; u < K_DMA; ++u) {
-      const __bf16* src = kt + (int64_t)min(k_slot[u] >> 16, last) * kv_row_elems_k + (k_slot[u] & 0xffff);
-      dma16(src, kl + (u * kWaves + wave) * 1024);
-    }
+      for (int u = 0; u < K_DMA; ++u) dma16_sv(kt, k_off[u], kl + (u * kWaves + wave) * 1024);
 #pragma unroll
-    for (int u = 0; u < V_DMA; ++u) {
-      const __bf16* src = vt + (int64_t)min(v_slot[u] >> 16, last) * kv_row_elems_v + (v_slot[u] & 0xffff);
-      dma16(src, vl + (u * kWaves + wave) * 1024);
+      for (int u = 0; u < V_DMA; ++u) dma16_sv(vt, v_off[u], vl + (u * kWaves + wave) * 1024);
+    } else {  // a chunk's partial last tile: rows past it re-read its last row (finite, masked)
+#pragma unroll
+      for (int u = 0; u < K_DMA; ++u)
+        dma16_sv(kt, (unsigned)(min(k_row[u], last) * kv_row_bytes_k) + k_col[u], kl + (u * kWaves + wave) * 1024);
+#pragma unroll
+      for (int u = 0; u < V_DMA; ++u)
+        dma16_sv(vt, (unsigned)(min(v_row[u], last) * kv_row_bytes_v) + v_col[u], vl + (u * kWaves + wave) * 1024);
     }
   };
 
   f32x16 oacc[C::MV];
 #pragma unroll
   for (int mv = 0; mv < C::MV; ++mv) oacc[mv] = f32x16{};
-  float m_run = -INFINITY;  // running max, log2 units (scaled logits)
+  // Running max of the row in log2 units (m_run) and the offset the scores are taken against
+  // (m_use: m_run, or 0 before the first visible key). The QK product of a tile starts from
+  // -m_use (cneg), so its outputs are already the exponents of the probabilities.
+  float m_run = -INFINITY, m_use = 0.f;
+  float thr = -INFINITY;    // raise the max when a tile's max exponent exceeds this
+  f32x16 cneg = f32x16{};   // -m_use in every entry
   float l_part = 0.f;       // this lane's share of the row sum
 
-  const float sl2 = p.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   TileCursor tc{0, 0};
@@ -293,11 +328,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     const char* kb = lds + buf * C::STAGE;
     const char* vb = kb + C::K_BYTES;
 
-    // ---- S^T = K Q^T for 64 keys (two 32-key blocks)
+    // ---- exponents x = K Q'^T - m_use for 64 keys (two 32-key blocks)
     f32x16 s[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      f32x16 acc = {};
+      f32x16 acc = cneg;
       const int krow = mb * 32 + (lane & 31);
       const char* kr = kb + krow * (C::KCH * 16);
       const int sw = swz<C::KCH>(krow);
@@ -322,34 +357,43 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     const int nvalid = min(kBK, c - tc.t0);
     const bool need_mask = (kpos0 + kBK - 1 > qmin) || (nvalid < kBK);
     if (need_mask) {
+      // key kk is visible iff kk <= lim (kk < nvalid and kpos0 + kk <= my_pos)
+      const int lim = min(nvalid - 1, my_pos - kpos0) - 4 * hl;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          int kk = mb * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
-          bool vis = (kk < nvalid) && (kpos0 + kk <= my_pos);
-          s[mb][r] = vis ? s[mb][r] : -INFINITY;
+          const int kk = mb * 32 + 8 * (r / 4) + (r % 4);  // minus the lane's 4*hl
+          s[mb][r] = kk <= lim ? s[mb][r] : -INFINITY;
         }
       }
     }
 
-    // ---- online softmax (row = lane & 31; this lane holds 32 of the row's 64 scores)
-    float mt = s[0][0];
+    // ---- online softmax (row = lane & 31; this lane holds 32 of the row's 64 exponents)
+    float mt = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[0][r]);
+    for (int r = 2; r < 16; ++r) mt = fmaxf(mt, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[1][r]);
-    mt = wave_max32(mt) * sl2;
-    const bool raise = mt > m_run + kRescaleSlack;
-    if (__any(raise)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_part *= alpha;
+    mt = wave_max32(mt);
+    if (__any(mt > thr)) {
+      // new max for the row; shift this tile's exponents and rescale what came before
+      const float m_new = fmaxf(m_run, m_use + mt);
+      if (m_new != -INFINITY) {
+        const float delta = m_new - m_use;
 #pragma unroll
-      for (int mv = 0; mv < C::MV; ++mv) oacc[mv] *= alpha;
-      m_run = m_new;
+        for (int mb = 0; mb < 2; ++mb) s[mb] -= delta;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+        l_part *= alpha;
+#pragma unroll
+        for (int mv = 0; mv < C::MV; ++mv) oacc[mv] *= alpha;
+        m_run = m_new;
+        m_use = m_new;
+        thr = kRescaleSlack;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cneg[r] = -m_new;
+      }
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
     // probabilities -> bf16 B operands (k-step ks uses registers 8*(ks%2).. of block ks/2)
     bf16x8 pb[4];
@@ -357,8 +401,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r], sl2, -m_use));
-        float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][r + 1], sl2, -m_use));
+        float e0 = __builtin_amdgcn_exp2f(s[mb][r]);
+        float e1 = __builtin_amdgcn_exp2f(s[mb][r + 1]);
         bf16x2 pr = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){e0, e1}, bf16x2);
         l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_part, false);
         const int ks = mb * 2 + r / 8;

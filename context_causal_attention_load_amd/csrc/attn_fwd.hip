@@ -172,8 +172,9 @@ struct TileCursor {
   int chunk, t0;
 };
 
+template <int BK = kBK>
 __device__ __forceinline__ void next_tile(TileCursor& tc, int c, int qmax) {
-  tc.t0 += kBK;
+  tc.t0 += BK;
   if (tc.t0 >= c || tc.chunk * c + tc.t0 > qmax) {
     tc.chunk += 1;
     tc.t0 = 0;
@@ -183,18 +184,22 @@ __device__ __forceinline__ void next_tile(TileCursor& tc, int c, int qmax) {
 // ------------------------------------------------------------------------------------------
 // bf16 kernel
 // ------------------------------------------------------------------------------------------
+// Keys per tile: 128 where two stages of K and V fit the 160 KB of LDS, else 64.
 template <int DQK, int DV>
 struct Bf16Cfg {
+  static constexpr int BK = (2 * 128 * (DQK + DV) * 2 <= 128 * 1024) ? 128 : 64;
   static constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
   static constexpr int VCH = DV / 8;
-  static constexpr int K_BYTES = kBK * KCH * 16;
-  static constexpr int V_BYTES = kBK * VCH * 16;
+  static constexpr int K_BYTES = BK * KCH * 16;
+  static constexpr int V_BYTES = BK * VCH * 16;
   static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int K_LOADS = kBK * KCH / kThreads;
-  static constexpr int V_LOADS = kBK * VCH / kThreads;
-  static_assert(kBK * KCH % kThreads == 0 && kBK * VCH % kThreads == 0, "tile/thread mismatch");
+  static constexpr int K_LOADS = BK * KCH / kThreads;
+  static constexpr int V_LOADS = BK * VCH / kThreads;
+  static_assert(BK * KCH % kThreads == 0 && BK * VCH % kThreads == 0, "tile/thread mismatch");
   static constexpr int QK_STEPS = DQK / 16;
   static constexpr int MV = DV / 32;
+  static constexpr int MB = BK / 32;   // 32-key blocks of S^T
+  static constexpr int PKS = BK / 16;  // k-steps of the P V product
 };
 
 template <int DQK, int DV>
@@ -273,12 +278,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   const unsigned lds0 = (unsigned)(uintptr_t)lds;
   auto dma_tile = [&](const TileCursor& tc, int b) {
     const int64_t prow0 = lb_chunk_offset(tc.chunk, c, p.cp) + tc.t0;
-    const int last = min(kBK, c - tc.t0) - 1;
+    const int last = min(C::BK, c - tc.t0) - 1;
     const char* kt = kbase + prow0 * kv_row_bytes_k;
     const char* vt = vbase + prow0 * kv_row_bytes_v;
     const unsigned kl = lds0 + b * C::STAGE;
     const unsigned vl = kl + C::K_BYTES;
-    if (last == kBK - 1) {
+    if (last == C::BK - 1) {
 #pragma unroll
       for (int u = 0; u < K_DMA; ++u) dma16_sv(kt, k_off[u], kl + (u * kWaves + wave) * 1024);
 #pragma unroll
@@ -321,17 +326,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
 
   while (tc.chunk <= imax) {
     TileCursor nx = tc;
-    next_tile(nx, c, qmax);
+    next_tile<C::BK>(nx, c, qmax);
     const bool has_next = nx.chunk <= imax;
     if (has_next) dma_tile(nx, buf ^ 1);  // that stage was last read in the previous iteration
 
     const char* kb = lds + buf * C::STAGE;
     const char* vb = kb + C::K_BYTES;
 
-    // ---- exponents x = K Q'^T - m_use for 64 keys (two 32-key blocks)
-    f32x16 s[2];
+    // ---- exponents x = K Q'^T - m_use for the tile's keys (32-key blocks)
+    f32x16 s[C::MB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < C::MB; ++mb) {
       f32x16 acc = cneg;
       const int krow = mb * 32 + (lane & 31);
       const char* kr = kb + krow * (C::KCH * 16);
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     // keep each K-fragment read two MFMAs ahead of its use
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * C::QK_STEPS - 2; ++i) {
+    for (int i = 0; i < C::MB * C::QK_STEPS - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -354,13 +359,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
 
     // ---- mask (only tiles that reach past the smallest query position, or partial tiles)
     const int kpos0 = tc.chunk * c + tc.t0;
-    const int nvalid = min(kBK, c - tc.t0);
-    const bool need_mask = (kpos0 + kBK - 1 > qmin) || (nvalid < kBK);
+    const int nvalid = min(C::BK, c - tc.t0);
+    const bool need_mask = (kpos0 + C::BK - 1 > qmin) || (nvalid < C::BK);
     if (need_mask) {
       // key kk is visible iff kk <= lim (kk < nvalid and kpos0 + kk <= my_pos)
       const int lim = min(nvalid - 1, my_pos - kpos0) - 4 * hl;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < C::MB; ++mb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk = mb * 32 + 8 * (r / 4) + (r % 4);  // minus the lane's 4*hl
@@ -369,12 +374,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
       }
     }
 
-    // ---- online softmax (row = lane & 31; this lane holds 32 of the row's 64 exponents)
+    // ---- online softmax (row = lane & 31; this lane holds half of the row's exponents)
     float mt = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int r = 2; r < 16; ++r) mt = fmaxf(mt, s[0][r]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[1][r]);
+    for (int mb = 1; mb < C::MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[mb][r]);
     mt = wave_max32(mt);
     if (__any(mt > thr)) {
       // new max for the row; shift this tile's exponents and rescale what came before
@@ -382,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
       if (m_new != -INFINITY) {
         const float delta = m_new - m_use;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) s[mb] -= delta;
+        for (int mb = 0; mb < C::MB; ++mb) s[mb] -= delta;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
         l_part *= alpha;
 #pragma unroll
@@ -396,9 +403,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     }
 
     // probabilities -> bf16 B operands (k-step ks uses registers 8*(ks%2).. of block ks/2)
-    bf16x8 pb[4];
+    bf16x8 pb[C::PKS];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < C::MB; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float e0 = __builtin_amdgcn_exp2f(s[mb][r]);
@@ -416,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
 #pragma unroll
     for (int mv = 0; mv < C::MV; ++mv) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < C::PKS; ++ks) {
         const int row_a = 16 * ks + 4 * (grp / 2) + tr_e;
         const int col = 32 * mv + 16 * (grp % 2) + 4 * tr_q;
         const int ch = col / 8, within = (col % 8) * 2;
@@ -436,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     // same for the transposed V reads (two per MFMA)
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 4 * C::MV - 2; ++i) {
+    for (int i = 0; i < C::PKS * C::MV - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }

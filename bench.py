@@ -10,6 +10,10 @@ step = the rank's whole share of the hot path, inputs resident in HBM:
   4. scatter O and LSE back to original token order.
 Step i runs rank i % cp, so the timed steps cover every rank; per-rank times are reported.
 
+After the timed steps (not part of them): every rank's attention kernel with the balanced
+shard and with a contiguous shard of the natural order, to show the spread the load balance
+removes (`load_balance`; skip with --no-balance-demo).
+
 Also measured: GQA decode (Mixtral-8x22B shape, batch 24, 48/8 heads, D 128, cache 2048 with
 lengths uniform in [1024, 2048]), rotating 4 cache copies so reads come from HBM rather than
 the 256 MB last-level cache; and the CPU fp64 oracle on a bounded row sample of the same
@@ -60,7 +64,7 @@ def useful_flops(seq, cp, hq, dqk, dv, batch=1):
     return 2.0 * pairs * hq * (dqk + dv) * batch
 
 
-def bench_prefill(w, cp, steps, warmup, dev):
+def bench_prefill(w, cp, steps, warmup, dev, balance_demo=True):
     import context_causal_attention_load_amd as cpa
     from context_causal_attention_load_amd import synth
 
@@ -107,9 +111,50 @@ def bench_prefill(w, cp, steps, warmup, dev):
     per_rank = {}
     for i in range(steps):
         per_rank.setdefault(i % cp, []).append(step_ms[i])
-    return dict(wall_s=wall, attn_ms=attn_ms, step_ms=step_ms,
-                per_rank_ms={r: sum(v) / len(v) for r, v in sorted(per_rank.items())},
-                flops=useful_flops(S, cp, w.hq, w.d_qk, w.d_v, w.batch))
+    out = dict(wall_s=wall, attn_ms=attn_ms, step_ms=step_ms,
+               per_rank_ms={r: sum(v) / len(v) for r, v in sorted(per_rank.items())},
+               flops=useful_flops(S, cp, w.hq, w.d_qk, w.d_v, w.batch))
+    if balance_demo:
+        out["balance"] = balance_demo_ms(w, cp, qd, kd, vd, kp, vp, q_shard, o_shard, lse_shard)
+    return out
+
+
+def balance_demo_ms(w, cp, qd, kd, vd, kp, vp, q_shard, o_shard, lse_shard):
+    """Outside the timed steps: every rank's attention kernel time with the load-balanced shard
+    (chunks r and 2cp-1-r) and with a contiguous shard (rows r*S/cp .. of the natural order,
+    K/V in natural order, given as explicit positions), one launch each after a warm-up."""
+    import context_causal_attention_load_amd as cpa
+
+    S, c = w.seq, w.seq // (2 * cp)
+
+    def timed(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    balanced, contiguous = [], []
+    for r in range(cp):
+        b0 = r * 2 * c
+        cpa.permute(qd, cp, row_begin=b0, row_count=2 * c, out=q_shard)
+        balanced.append(timed(lambda: cpa.attention_fwd(q_shard, kp, vp, cp, r, scale=w.scale, out=o_shard,
+                                                        lse=lse_shard)))
+        rows = torch.arange(b0, b0 + 2 * c, dtype=torch.int32, device=qd.device)
+        q_rows = qd[:, b0:b0 + 2 * c]
+        contiguous.append(timed(lambda: cpa.attention_fwd(q_rows, kd, vd, 1, 0, q_positions=rows, scale=w.scale,
+                                                          out=o_shard, lse=lse_shard)))
+
+    def spread(v):
+        return max(v) / (sum(v) / len(v))
+
+    return {"balanced_attn_ms_per_rank": [round(x, 3) for x in balanced],
+            "contiguous_attn_ms_per_rank": [round(x, 3) for x in contiguous],
+            "balanced_max_over_mean": round(spread(balanced), 4),
+            "contiguous_max_over_mean": round(spread(contiguous), 4),
+            "contiguous_max_over_mean_closed_form": round((2 * cp - 1) / cp, 4)}
 
 
 def bench_decode(w, iters, dev, copies=4):
@@ -181,6 +226,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-balance-demo", action="store_true",
+                    help="skip the per-rank balanced vs contiguous shard timing (after the timed steps)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share (one context-parallel rank); runs on more than one GPU "
@@ -195,7 +242,7 @@ def main():
     dev = "cuda:0"
     w = synth.LLAMA31_70B_S131K
     cp = w.cps[0]
-    pre = bench_prefill(w, cp, args.steps, args.warmup, dev)
+    pre = bench_prefill(w, cp, args.steps, args.warmup, dev, balance_demo=not args.no_balance_demo)
     ms_per_step = sum(pre["step_ms"]) / len(pre["step_ms"])
     value = pre["flops"] / (ms_per_step * 1e-3) / 1e12
     attn_avg_ms = sum(pre["attn_ms"]) / len(pre["attn_ms"])
@@ -225,6 +272,8 @@ def main():
                      "useful_flop_per_launch": pre["flops"]},
         "per_rank_step_ms": {str(r): round(t, 3) for r, t in pre["per_rank_ms"].items()},
     }
+    if "balance" in pre:
+        result["load_balance"] = pre["balance"]
     if not args.no_decode:
         dw = synth.MIXTRAL_8X22B_DECODE
         d = bench_decode(dw, args.decode_iters, dev)

@@ -240,6 +240,37 @@ def full_workload(w):
     return _FULL[w.name]
 
 
+@pytest.mark.parametrize("cp", synth.LLAMA2_7B_S8K.cps)
+def test_attention_llama7b_every_row(cp):
+    """8192-token Llama2-7B-shaped MHA: the complete O and LSE of every rank (every row, every
+    head) against the oracle, at cp = 1 (natural order) and at cp = 4 (load-balanced shards)."""
+    w = synth.LLAMA2_7B_S8K
+    pf = full_workload(w)
+    for rank in range(cp):
+        check_rank(pf, cp, rank, rows=None, tag=w.name)
+
+
+def test_attention_contiguous_shards_llama7b():
+    """The unbalanced (contiguous) layout the load balance replaces: rank r's rows are
+    r*S/cp .. of the natural order and K/V stay in natural order (the call's cp = 1 order with
+    explicit positions). Sampled rows of every rank of cp = 4 against plain causal attention."""
+    w = synth.LLAMA2_7B_S8K
+    pf = full_workload(w)
+    cp, S = 4, w.seq
+    k_nat, v_nat = pf.k.double(), pf.v.double()
+    kpos = np.arange(S)
+    for r in range(cp):
+        b0, n = r * S // cp, S // cp
+        rows = torch.arange(b0, b0 + n, dtype=torch.int32)
+        announce(f"contiguous shard r={r} rows {b0}..{b0 + n - 1}")
+        o, lse = cpa.attention_fwd(pf.qd[:, b0:b0 + n], pf.kd, pf.vd, 1, 0, q_positions=rows.to(DEV), scale=pf.scale)
+        torch.cuda.synchronize()
+        pick = sample_rows(n // 2, 24, seed=77 + r)
+        O_ref, L_ref = oatt.causal_attention_ref(pf.q[:, b0 + pick], k_nat, v_nat, (b0 + pick), kpos, pf.scale)
+        assert_close(o[:, pick].float().cpu().numpy(), O_ref, TOL[pf.dtype], f"contiguous O r={r}")
+        assert_close(lse[:, :, pick].cpu().numpy(), L_ref, TOL[pf.dtype], f"contiguous LSE r={r}")
+
+
 FULL_CASES = [(w, cp, r) for w in (synth.LLAMA2_7B_S8K, synth.DEEPSEEK_V3_MLA_S32K, synth.LLAMA31_70B_S131K)
               for cp in w.cps for r in range(cp)]
 

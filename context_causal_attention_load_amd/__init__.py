@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     unpermute,
     attention_fwd,
     decode,
+    decode_merge,
     decode_workspace_bytes,
     lb_source_index,
     lb_positions,

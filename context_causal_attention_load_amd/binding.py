@@ -61,6 +61,8 @@ def load_library():
     lib.gqa_decode_attention.restype = ctypes.c_int
     lib.gqa_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                          vp, ctypes.c_size_t, vp]
+    lib.gqa_decode_merge.restype = ctypes.c_int
+    lib.gqa_decode_merge.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     _lib = lib
     return lib
 
@@ -214,4 +216,24 @@ def decode(q, k_cache, v_cache, lengths, scale=None, workspace=None, out=None, l
                                                _ptr(lse), B, Hq, Hkv, D, Lmax, _DTYPES[q.dtype], float(scale),
                                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                                _stream(q.device)))
+    return out, lse
+
+
+def decode_merge(o_parts, lse_parts, out=None, lse=None, want_lse=True):
+    """Combine decode results of disjoint cache slices (a cache sharded along its length).
+    o_parts [R, B, Hq, D]; lse_parts [R, B, Hq] fp32 (natural log, -inf = empty slice).
+    Returns (O [B, Hq, D], LSE [B, Hq] fp32)."""
+    _need_gpu(o_parts, lse_parts, out, lse)
+    if o_parts.dtype not in _DTYPES:
+        raise ValueError("o_parts must be float32 or bfloat16")
+    R, B, Hq, D = o_parts.shape
+    if lse_parts.dtype != torch.float32 or tuple(lse_parts.shape) != (R, B, Hq):
+        raise ValueError("lse_parts must be float32 [R, B, Hq]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=o_parts.dtype, device=o_parts.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=o_parts.device)
+    _check("gqa_decode_merge",
+           load_library().gqa_decode_merge(_ptr(o_parts), _ptr(lse_parts), _ptr(out), _ptr(lse), R, B, Hq, D,
+                                           _DTYPES[o_parts.dtype], _stream(o_parts.device)))
     return out, lse

@@ -242,4 +242,36 @@ int gqa_decode_attention(const void* q, const void* k_cache, const void* v_cache
   return CPA_OK;
 }
 
+int gqa_decode_merge(const void* o_parts, const float* lse_parts, void* o, float* lse, int32_t parts,
+                     int32_t batch, int32_t hq, int32_t d, int32_t dtype, void* stream) {
+  const char* where = "gqa_decode_merge";
+  if (parts < 1) return fail(CPA_EINVAL, "%s: parts must be >= 1", where);
+  if (batch < 0 || hq < 0) return fail(CPA_EINVAL, "%s: batch and hq must be >= 0", where);
+  if (d < 1) return fail(CPA_EINVAL, "%s: d must be >= 1", where);
+  if (dtype != CPA_F32 && dtype != CPA_BF16) return fail(CPA_EINVAL, "%s: unknown dtype %d", where, dtype);
+  if (batch == 0 || hq == 0) return CPA_OK;
+  if ((int64_t)batch * hq >= (int64_t(1) << 31)) return fail(CPA_EINVAL, "%s: batch * hq too large", where);
+  if ((int64_t)parts * batch * hq * d >= (int64_t(1) << 40)) return fail(CPA_EINVAL, "%s: parts too large", where);
+  if (!o_parts || !lse_parts || !o) return fail(CPA_EINVAL, "%s: null pointer", where);
+  const uintptr_t elem = dtype == CPA_BF16 ? 1u : 3u;
+  if (((uintptr_t)o_parts & elem) || ((uintptr_t)o & elem) || ((uintptr_t)lse_parts & 3u) ||
+      (lse && ((uintptr_t)lse & 3u)))
+    return fail(CPA_EINVAL, "%s: pointers must be aligned to their element size", where);
+  int rc = check_device(where);
+  if (rc) return rc;
+  DecodeMergeArgs a;
+  a.o_parts = o_parts;
+  a.lse_parts = lse_parts;
+  a.o = o;
+  a.lse = lse;
+  a.parts = parts;
+  a.batch = batch;
+  a.hq = hq;
+  a.d = d;
+  a.bf16 = dtype == CPA_BF16;
+  hipError_t e = launch_decode_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, where);
+  return CPA_OK;
+}
+
 }  // extern "C"

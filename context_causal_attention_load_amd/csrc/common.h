@@ -67,6 +67,16 @@ struct DecodeArgs {
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 
+struct DecodeMergeArgs {
+  const void* o_parts;     // [parts, batch, hq, d]
+  const float* lse_parts;  // [parts, batch, hq]
+  void* o;                 // [batch, hq, d]
+  float* lse;              // [batch, hq], may be null
+  int parts, batch, hq, d;
+  bool bf16;
+};
+hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream);
+
 // Decode split geometry, shared by the workspace-size query and the launcher. The workspace
 // holds the split partials [batch, hq, nsplit, d + 2] in float32: d unnormalised outputs, then
 // the split's max and sum (log2 units).

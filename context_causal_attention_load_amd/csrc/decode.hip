@@ -249,9 +249,39 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
       acc = __builtin_fmaf(w, part[s * (D + 2) + d], acc);
     }
   }
+  // a sequence of length 0 has no key: output 0 and log-sum-exp ln 0 = -inf
+  const bool empty = !(L > 0.f);
   T* out = static_cast<T*>(p.o) + (int64_t)bh * D;
-  out[d] = (T)(acc / L);
-  if (p.lse && d == 0) p.lse[bh] = (M + __builtin_amdgcn_logf(L)) * kLn2;
+  out[d] = empty ? (T)0.f : (T)(acc / L);
+  if (p.lse && d == 0) p.lse[bh] = empty ? -INFINITY : (M + __builtin_amdgcn_logf(L)) * kLn2;
+}
+
+// Merge of decode results computed over disjoint slices of every sequence's keys (the shards of
+// a cache split along its length): block (b, h); O = sum_r w_r o_r / sum_r w_r and
+// LSE = M + ln sum_r w_r with w_r = exp(lse_r - M), M = max_r lse_r. A part whose log-sum-exp
+// is -inf (an empty slice) has weight 0 and its output is not read into the sum.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_lse_merge_kernel(const T* __restrict__ o_parts,
+                                                               const float* __restrict__ lse_parts, T* __restrict__ out,
+                                                               float* __restrict__ lse_out, int R, int64_t BH, int D) {
+  const int64_t bh = blockIdx.x;
+  float M = -INFINITY;
+  for (int r = 0; r < R; ++r) M = fmaxf(M, lse_parts[r * BH + bh]);
+  const bool empty = M == -INFINITY;
+  float L = 0.f;
+  if (!empty)
+    for (int r = 0; r < R; ++r) L += __builtin_amdgcn_exp2f((lse_parts[r * BH + bh] - M) * kLog2e);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float acc = 0.f;
+    if (!empty) {
+      for (int r = 0; r < R; ++r) {
+        const float lr = lse_parts[r * BH + bh];
+        if (lr != -INFINITY) acc += __builtin_amdgcn_exp2f((lr - M) * kLog2e) * to_float(o_parts[(r * BH + bh) * D + d]);
+      }
+    }
+    out[bh * D + d] = empty ? (T)0.f : (T)(acc / L);
+  }
+  if (lse_out && threadIdx.x == 0) lse_out[bh] = empty ? -INFINITY : M + __builtin_amdgcn_logf(L) * kLn2;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -512,5 +542,21 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch_typed<__bf16>(a, stream); }
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) { return launch_typed<float>(a, stream); }
+
+hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream) {
+  const int64_t bh = (int64_t)a.batch * a.hq;
+  if (bh == 0) return hipSuccess;
+  const int threads = a.d >= 256 ? 256 : ((a.d + 63) / 64) * 64;
+  if (a.bf16) {
+    hipLaunchKernelGGL(decode_lse_merge_kernel<__bf16>, dim3((unsigned)bh), dim3(threads), 0, stream,
+                       static_cast<const __bf16*>(a.o_parts), a.lse_parts, static_cast<__bf16*>(a.o), a.lse, a.parts, bh,
+                       a.d);
+  } else {
+    hipLaunchKernelGGL(decode_lse_merge_kernel<float>, dim3((unsigned)bh), dim3(threads), 0, stream,
+                       static_cast<const float*>(a.o_parts), a.lse_parts, static_cast<float*>(a.o), a.lse, a.parts, bh,
+                       a.d);
+  }
+  return hipGetLastError();
+}
 
 }  // namespace cpattn

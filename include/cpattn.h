@@ -139,7 +139,8 @@ int cp_attention_fwd(const void* q_shard, const void* k, const void* v,
  *   k_cache  [B, Hkv, max_len, D]   (each (b, kv head) slab contiguous)
  *   v_cache  [B, Hkv, max_len, D]
  *   lengths  [B] int32 (device), valid entries per sequence; device precondition
- *            1 <= lengths[b] <= max_len. Entries at index >= lengths[b] are never read.
+ *            0 <= lengths[b] <= max_len. Entries at index >= lengths[b] are never read. A
+ *            length of 0 (an empty cache slice) gives O = 0 and LSE = -inf.
  *   o        [B, Hq, D] same dtype as q (output)
  *   lse      [B, Hq] float32 (output, may be NULL)
  *   workspace, workspace_bytes: device scratch of at least gqa_decode_workspace_bytes(...)
@@ -154,6 +155,24 @@ int gqa_decode_attention(const void* q, const void* k_cache, const void* v_cache
                          int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t max_len,
                          int32_t dtype, float softmax_scale,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Merge of decode results over a cache split along its length ("rename context to
+ * context_autoregressive", PR 1453, Description: a separate context-parallel axis for
+ * autoregressive inference, which shards the cache by length). Each of `parts` shards holds a
+ * disjoint slice of every sequence's cache entries and runs gqa_decode_attention on it; this call
+ * combines their results exactly as one decode over the whole cache would:
+ *   M = max_r lse_r,  w_r = exp(lse_r - M),  O = sum_r w_r o_r / sum_r w_r,  LSE = M + ln sum_r w_r.
+ *
+ *   o_parts   [parts, B, Hq, D] in dtype (device), each part's normalised output
+ *   lse_parts [parts, B, Hq] float32 (device), each part's natural-log LSE; -inf marks an empty
+ *             slice (weight 0; its o_parts entries are not read into the sum)
+ *   o         [B, Hq, D] in dtype (output); lse [B, Hq] float32 (output, may be NULL)
+ * A (b, h) with every part empty gets O = 0 and LSE = -inf. o may not overlap o_parts.
+ * CPA_EINVAL for parts < 1, negative sizes, d < 1, an unknown dtype, a null pointer or a pointer
+ * not aligned to its element size. */
+int gqa_decode_merge(const void* o_parts, const float* lse_parts, void* o, float* lse, int32_t parts,
+                     int32_t batch, int32_t hq, int32_t d, int32_t dtype, void* stream);
 
 #ifdef __cplusplus
 }

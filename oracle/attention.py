@@ -113,6 +113,8 @@ def decode_ref(q, k_cache, v_cache, lengths, scale):
     q: [B, Hq, D]; k_cache, v_cache: [B, Hkv, Lmax, D] (cache laid out head-major, each
     (b, kv head) slab contiguous); lengths: [B] valid entries per sequence.
     Entries at index >= lengths[b] are never read, so they may hold anything (NaN included).
+    A length of 0 (an empty slice of a cache split along its length) has no key: its
+    log-sum-exp is ln 0 = -inf and its output is taken as 0 (a merge gives it weight 0).
     Returns (O [B, Hq, Dv] float64, LSE [B, Hq] float64).
     """
     q64 = _f64(q)
@@ -125,8 +127,12 @@ def decode_ref(q, k_cache, v_cache, lengths, scale):
     lse = np.empty((B, Hq))
     for b in range(B):
         n = lengths[b]
-        if n < 1:
-            raise ValueError("every sequence needs at least one cached token")
+        if n < 0:
+            raise ValueError("lengths must be >= 0")
+        if n == 0:
+            out[b] = 0.0
+            lse[b] = -np.inf
+            continue
         for g in range(Hkv):
             kk = _f64(k_cache[b, g, :n])
             vv = _f64(v_cache[b, g, :n])
@@ -137,6 +143,33 @@ def decode_ref(q, k_cache, v_cache, lengths, scale):
                 l = p.sum()
                 out[b, h] = (p @ vv) / l
                 lse[b, h] = m + np.log(l)
+    return out, lse
+
+
+def decode_merge_ref(o_parts, lse_parts):
+    """Combine decode results over disjoint slices of the keys ("rename context to
+    context_autoregressive", PR 1453: inference context parallelism shards the cache along its
+    length). With parts r: M = max_r lse_r, w_r = exp(lse_r - M),
+    O = sum_r w_r o_r / sum_r w_r, LSE = M + ln sum_r w_r. Parts with lse = -inf carry no keys and
+    are left out; if all are, O = 0 and LSE = -inf.
+
+    o_parts: [R, B, Hq, Dv]; lse_parts: [R, B, Hq]. Returns (O [B, Hq, Dv], LSE [B, Hq]) float64.
+    """
+    o = _f64(o_parts)
+    l = _f64(lse_parts)
+    R, B, Hq, Dv = o.shape
+    out = np.zeros((B, Hq, Dv))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            live = [r for r in range(R) if l[r, b, h] != -np.inf]
+            if not live:
+                continue
+            m = max(l[r, b, h] for r in live)
+            w = {r: np.exp(l[r, b, h] - m) for r in live}
+            tot = sum(w.values())
+            out[b, h] = sum(w[r] * o[r, b, h] for r in live) / tot
+            lse[b, h] = m + np.log(tot)
     return out, lse
 
 

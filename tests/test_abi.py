@@ -153,6 +153,33 @@ def test_decode_argument_errors(lib, kw, status, substr):
     assert rc == status and substr in msg, (rc, msg)
 
 
+def _merge(lib, **kw):
+    a = dict(o_parts=FAKE, lse_parts=FAKE, o=FAKE, lse=None, parts=4, batch=24, hq=48, d=128, dtype=binding.CPA_BF16)
+    a.update(kw)
+    rc = lib.gqa_decode_merge(a["o_parts"], a["lse_parts"], a["o"], a["lse"], a["parts"], a["batch"], a["hq"], a["d"],
+                              a["dtype"], None)
+    return _status_and_message(lib, rc)
+
+
+@pytest.mark.parametrize("kw,status,substr", [
+    (dict(parts=0), binding.CPA_EINVAL, "parts"),
+    (dict(batch=-1), binding.CPA_EINVAL, ">= 0"),
+    (dict(d=0), binding.CPA_EINVAL, "d must"),
+    (dict(dtype=7), binding.CPA_EINVAL, "dtype"),
+    (dict(o=None), binding.CPA_EINVAL, "null"),
+    (dict(lse_parts=ctypes.c_void_p(4098)), binding.CPA_EINVAL, "aligned"),
+    (dict(o_parts=ctypes.c_void_p(4097)), binding.CPA_EINVAL, "aligned"),
+])
+def test_decode_merge_argument_errors(lib, kw, status, substr):
+    rc, msg = _merge(lib, **kw)
+    assert rc == status and substr in msg, (rc, msg)
+
+
+def test_decode_merge_empty_is_ok_without_device(lib):
+    assert _merge(lib, batch=0)[0] == 0
+    assert _merge(lib, hq=0)[0] == 0
+
+
 def test_decode_workspace_size(lib):
     # (max, sum, D outputs) per (sequence, query head, split of 256 keys)
     assert cpa.decode_workspace_bytes(24, 48, 8, 2048, 128) == 24 * 48 * 8 * 130 * 4

@@ -349,6 +349,48 @@ def test_decode_edge_lengths(batch, hq, hkv, d, max_len, dtype, lens):
     assert_close(lse, L_ref, tol, "decode LSE")
 
 
+def test_decode_zero_length():
+    """A length of 0 (an empty cache slice) gives O = 0 and LSE = -inf; other rows unchanged."""
+    announce("decode with a zero length")
+    lengths, q, kc, vc = synth.decode_inputs(3, 12, 4, 128, 300, 1, 300, torch.bfloat16, seed=9)
+    lengths = torch.tensor([0, 300, 41], dtype=torch.int32)
+    o, lse = run_decode(lengths, q, kc, vc, 1.0 / math.sqrt(128))
+    assert np.all(np.asarray(o)[0] == 0.0) and np.all(np.asarray(lse)[0] == -np.inf)
+    O_ref, L_ref = oatt.decode_ref(q, kc, vc, lengths.numpy(), 1.0 / math.sqrt(128))
+    assert_close(np.asarray(o)[1:], O_ref[1:], 2e-2, "decode O (non-empty rows)")
+    assert_close(np.asarray(lse)[1:], L_ref[1:], 2e-2, "decode LSE (non-empty rows)")
+
+
+@pytest.mark.parametrize("shape", ["mixtral-8x22b-b24", "fp32-small"])
+def test_decode_length_sharded_merge(shape):
+    """A cache split along its length into R shards (inference context parallelism): decode on
+    each shard's own cache slice, then gqa_decode_merge, against one oracle decode over the whole
+    cache. Short sequences leave later shards empty."""
+    if shape == "mixtral-8x22b-b24":
+        w = synth.MIXTRAL_8X22B_DECODE
+        lengths, q, kc, vc = synth.workload_decode_inputs(w)
+        scale, R, tol = w.scale, 4, 2e-2
+    else:
+        lengths, q, kc, vc = synth.decode_inputs(3, 8, 2, 64, 96, 1, 96, torch.float32, seed=13)
+        lengths = torch.tensor([96, 33, 5], dtype=torch.int32)
+        scale, R, tol = 0.125, 3, 1e-4
+    Lmax = kc.shape[2]
+    W = Lmax // R
+    announce(f"length-sharded decode {shape}: {R} shards of {W}")
+    o_parts, l_parts = [], []
+    for r in range(R):
+        n = torch.clamp(lengths - r * W, 0, W).to(torch.int32)
+        o, lse = cpa.decode(q.to(DEV), kc[:, :, r * W:(r + 1) * W].contiguous().to(DEV),
+                            vc[:, :, r * W:(r + 1) * W].contiguous().to(DEV), n.to(DEV), scale=scale)
+        o_parts.append(o)
+        l_parts.append(lse)
+    O, L = cpa.decode_merge(torch.stack(o_parts), torch.stack(l_parts))
+    torch.cuda.synchronize()
+    O_ref, L_ref = oatt.decode_ref(q, kc, vc, lengths.numpy(), scale)
+    assert_close(O.float().cpu().numpy(), O_ref, tol, f"sharded decode O ({shape})")
+    assert_close(L.cpu().numpy(), L_ref, tol, f"sharded decode LSE ({shape})")
+
+
 def test_decode_workspace_reuse():
     """One workspace (garbage-filled) serves repeated calls and a smaller batch afterwards."""
     announce("decode workspace reuse")

@@ -309,6 +309,64 @@ def test_decode_pins():
     _check_decode(oatt.decode_ref)
 
 
+def test_decode_empty_length():
+    """A length-0 sequence (an empty slice of a cache split along its length) has LSE = ln 0 =
+    -inf and output 0; the other sequences are unaffected."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 4, 8))
+    kc = rng.standard_normal((2, 2, 6, 8))
+    vc = rng.standard_normal((2, 2, 6, 8))
+    O, L = oatt.decode_ref(q, kc, vc, [0, 5], 0.3)
+    assert np.all(O[0] == 0.0) and np.all(L[0] == -np.inf)
+    O1, L1 = oatt.decode_ref(q[1:], kc[1:], vc[1:], [5], 0.3)
+    np.testing.assert_array_equal(O[1], O1[0])
+    np.testing.assert_array_equal(L[1], L1[0])
+
+
+def _check_merge(merge_fn):
+    """Split invariance: decoding disjoint slices of each cache and merging the results equals
+    one decode over the whole cache (slices include empty ones); plus closed forms."""
+    B, Hq, Hkv, D, Lmax, W = 3, 4, 2, 8, 40, 16
+    rng = np.random.default_rng(31)
+    lengths = np.array([40, 17, 1])
+    q = rng.standard_normal((B, Hq, D))
+    kc = rng.standard_normal((B, Hkv, Lmax, D))
+    vc = rng.standard_normal((B, Hkv, Lmax, D))
+    scale = 0.3
+    parts_o, parts_l = [], []
+    for start in range(0, Lmax, W):
+        width = min(W, Lmax - start)
+        n = np.clip(lengths - start, 0, width)
+        o, l = oatt.decode_ref(q, kc[:, :, start:start + width], vc[:, :, start:start + width], n, scale)
+        parts_o.append(o)
+        parts_l.append(l)
+    O, L = merge_fn(np.stack(parts_o), np.stack(parts_l))
+    O_full, L_full = oatt.decode_ref(q, kc, vc, lengths, scale)
+    np.testing.assert_allclose(O, O_full, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, L_full, rtol=0, atol=1e-12)
+    # the same result from the library routine over each valid prefix
+    for b in range(B):
+        n = lengths[b]
+        tk = torch.from_numpy(kc[b, :, :n]).repeat_interleave(Hq // Hkv, 0)
+        tv = torch.from_numpy(vc[b, :, :n]).repeat_interleave(Hq // Hkv, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q[b][:, None, :]), tk, tv, scale=scale)
+        np.testing.assert_allclose(O[b], ref[:, 0].numpy(), rtol=0, atol=1e-12)
+    # closed forms: one part is the identity; two equal parts keep O and add ln 2 to the LSE;
+    # all parts empty give O = 0 and LSE = -inf
+    O1, L1 = merge_fn(O_full[None], L_full[None])
+    np.testing.assert_allclose(O1, O_full, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(L1, L_full, rtol=0, atol=1e-15)
+    O2, L2 = merge_fn(np.stack([O_full, O_full]), np.stack([L_full, L_full]))
+    np.testing.assert_allclose(O2, O_full, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(L2, L_full + math.log(2.0), rtol=0, atol=1e-12)
+    O3, L3 = merge_fn(np.zeros((2, B, Hq, D)), np.full((2, B, Hq), -np.inf))
+    assert np.all(O3 == 0.0) and np.all(L3 == -np.inf)
+
+
+def test_decode_merge_pins():
+    _check_merge(oatt.decode_merge_ref)
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 
 def _perm_swapped_chunk_order(seq, cp):
@@ -353,6 +411,17 @@ def _dec_off_by_one(q, kc, vc, lengths, scale):
     return oatt.decode_ref(q, kc, vc, np.asarray(lengths) - 1 + (np.asarray(lengths) == 1), scale)
 
 
+def _merge_unweighted(o_parts, lse_parts):
+    # averages the live parts' outputs instead of weighting them by exp(lse)
+    o, l = np.asarray(o_parts, dtype=np.float64), np.asarray(lse_parts, dtype=np.float64)
+    live = l != -np.inf
+    cnt = np.maximum(live.sum(0), 1)
+    O = np.where(live[..., None], o, 0.0).sum(0) / cnt[..., None]
+    m = np.where(live, l, -np.inf).max(0)
+    L = np.where(np.isfinite(m), m + np.log(np.where(live, np.exp(l - np.where(np.isfinite(m), m, 0)), 0).sum(0)), -np.inf)
+    return O, L
+
+
 @pytest.mark.parametrize("check", [
     lambda: _check_golden(_perm_swapped_chunk_order),
     lambda: _check_balance(_perm_unbalanced, 64, 4),
@@ -361,7 +430,9 @@ def _dec_off_by_one(q, kc, vc, lengths, scale):
     lambda: _check_library(_att_wrong_group, 64, 2, 4, 2, 16, 16, 3),
     lambda: _check_brute(_att_transposed_v, 8, 2, 2, 1, 4, 4, 3),
     lambda: _check_decode(_dec_off_by_one),
-], ids=["chunk-order", "unbalanced", "strict-mask", "no-scale", "wrong-group", "mirrored-v", "decode-length"])
+    lambda: _check_merge(_merge_unweighted),
+], ids=["chunk-order", "unbalanced", "strict-mask", "no-scale", "wrong-group", "mirrored-v", "decode-length",
+        "merge-unweighted"])
 def test_planted_mistakes_are_caught(check):
     with pytest.raises((AssertionError, ValueError, IndexError)):
         check()

@@ -18,7 +18,10 @@ float32 N(0,1) in natural token order, token chunk by token chunk (``TOKEN_CHUNK
 per draw, all batches of a chunk at once), then rounded to the workload dtype with
 round-to-nearest-even (``Tensor.to``). Decode draws ``lengths`` (uniform integers in
 [len_min, len_max]) first, then q, then the K cache and the V cache over the full maximum
-length.
+length. The int8-cache decode draws ``lengths`` and q the same way, then for K and then V
+the codes (float32 N(0,1) times 40, rounded, clipped to [-127, 127]: the spread of absmax-int8
+codes of Gaussian rows) and then one positive float32 scale per cached row, uniform in
+[2.5/127, 3.5/127] (the absmax of 128 N(0,1) values divided by 127).
 """
 
 from dataclasses import dataclass, field
@@ -108,6 +111,29 @@ def decode_inputs(batch, hq, hkv, d, max_len, len_min, len_max, dtype, seed):
     k_cache = _draw(gen, (batch, hkv, max_len, d), dtype, token_axis=2)
     v_cache = _draw(gen, (batch, hkv, max_len, d), dtype, token_axis=2)
     return lengths, q, k_cache, v_cache
+
+
+def decode_int8_inputs(batch, hq, hkv, d, max_len, len_min, len_max, seed):
+    """lengths [B] int32, q [B,Hq,D] bf16, then (codes int8 [B,Hkv,Lmax,D], scales float32
+    [B,Hkv,Lmax]) for K and for V (CPU tensors)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    lengths = torch.randint(len_min, len_max + 1, (batch,), generator=gen, dtype=torch.int64).to(torch.int32)
+    q = torch.randn((batch, hq, d), generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    out = []
+    for _ in range(2):
+        codes = torch.empty((batch, hkv, max_len, d), dtype=torch.int8)
+        for t0 in range(0, max_len, TOKEN_CHUNK):
+            t1 = min(max_len, t0 + TOKEN_CHUNK)
+            block = torch.randn((batch, hkv, t1 - t0, d), generator=gen, dtype=torch.float32)
+            codes[:, :, t0:t1] = (block * 40).round().clamp(-127, 127).to(torch.int8)
+        scales = (torch.rand((batch, hkv, max_len), generator=gen, dtype=torch.float32) + 2.5) / 127
+        out += [codes, scales]
+    return (lengths, q, *out)
+
+
+def workload_decode_int8_inputs(w: DecodeWorkload, seed=None):
+    return decode_int8_inputs(w.batch, w.hq, w.hkv, w.d, w.max_len, w.len_min, w.len_max,
+                              w.seed if seed is None else seed)
 
 
 def workload_decode_inputs(w: DecodeWorkload, seed=None):

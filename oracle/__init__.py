@@ -17,6 +17,10 @@ Sources (web pages, cited by title and section):
 * "Add Pallas GPU decode attention in Maxtext inference" (MaxText PR 1066), Description /
   Tests: grouped-query single-token decode attention over a KV cache filled to the current
   length.
+* "rename context to context_autoregressive" (MaxText PR 1453), Description: inference
+  context parallelism splits the cache along its length (merge of per-slice decodes), and the
+  decode benchmark quantizes the KV cache to int8 (``oracle.quant``: the absmax per-row
+  reading taken for it).
 
 Every function computes in float64 from inputs upcast exactly from their stored dtype.
 
@@ -37,9 +41,11 @@ from .attention import (
     causal_attention_ref,
     cp_attention_ref,
     decode_ref,
+    decode_merge_ref,
     permute_ref,
     unpermute_ref,
 )
+from .quant import kv_quantize_ref, dequantize_ref, decode_int8_ref
 
 __all__ = [
     "load_balance_perm",
@@ -51,6 +57,10 @@ __all__ = [
     "causal_attention_ref",
     "cp_attention_ref",
     "decode_ref",
+    "decode_merge_ref",
+    "kv_quantize_ref",
+    "dequantize_ref",
+    "decode_int8_ref",
     "permute_ref",
     "unpermute_ref",
 ]

@@ -16,6 +16,7 @@ import torch
 import oracle
 from oracle import attention as oatt
 from oracle import lb_index as olb
+from oracle import quant as oq
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -367,6 +368,120 @@ def test_decode_merge_pins():
     _check_merge(oatt.decode_merge_ref)
 
 
+# ----------------------------------------------------------------------------- int8 cache pins
+
+def _read_quant_golden():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "kv_quant_rows.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        xs, cs, sc = (f.split() for f in line.split("|"))
+        rows.append((np.array([float(t) for t in xs], dtype=np.float32), np.array([int(t) for t in cs]),
+                     float.fromhex(sc[0])))
+    return rows
+
+
+def _check_quant_golden(quant_fn):
+    for x, codes, scale in _read_quant_golden():
+        c, s = quant_fn(x[None])
+        assert np.array_equal(np.asarray(c)[0].astype(np.int64), codes), (x, c, codes)
+        assert float(np.asarray(s)[0]) == scale, (x, s, scale)
+
+
+def test_quantize_golden_rows():
+    _check_quant_golden(oq.kv_quantize_ref)
+
+
+def _check_quant_invariants(quant_fn):
+    """Any correct absmax quantizer: codes in [-127, 127]; the largest |x| of a row maps to
+    +-127; every code is the nearest integer to x / scale (within float32 rounding of the
+    quotient); dequantized values are within half a step of x."""
+    rng = np.random.default_rng(41)
+    x = torch.from_numpy(rng.standard_normal((64, 128)) * rng.uniform(0.01, 50, (64, 1))).to(torch.bfloat16)
+    c, s = quant_fn(x)
+    c = np.asarray(c).astype(np.float64)
+    s = np.asarray(s).astype(np.float64)
+    xf = x.double().numpy()
+    assert c.min() >= -127 and c.max() <= 127
+    arg = np.abs(xf).argmax(1)
+    assert np.all(np.abs(c[np.arange(64), arg]) == 127)
+    assert np.all(np.sign(c[np.arange(64), arg]) == np.sign(xf[np.arange(64), arg]))
+    np.testing.assert_allclose(s, np.abs(xf).max(1) / 127, rtol=2 ** -23, atol=0)
+    assert np.all(np.abs(xf / s[:, None] - c) <= 0.5 + 1e-5)
+    assert np.all(np.abs(xf - c * s[:, None]) <= s[:, None] * (0.5 + 1e-5))
+
+
+def test_quantize_invariants():
+    _check_quant_invariants(oq.kv_quantize_ref)
+
+
+def _check_decode_int8(dec_fn):
+    """Closed forms of decode over a quantized cache (values code * scale)."""
+    rng = np.random.default_rng(43)
+    B, Hq, Hkv, D, Lmax = 2, 4, 2, 8, 6
+    q = rng.standard_normal((B, Hq, D))
+    kq = rng.integers(-127, 128, (B, Hkv, Lmax, D)).astype(np.int8)
+    vq = rng.integers(-127, 128, (B, Hkv, Lmax, D)).astype(np.int8)
+    ks = rng.uniform(0.001, 0.02, (B, Hkv, Lmax)).astype(np.float32)
+    vs = rng.uniform(0.5, 2.0, (B, Hkv, Lmax)).astype(np.float32)
+    sm = 0.3
+    # one key: O is that key's value, LSE its scaled logit
+    O, L = dec_fn(q, kq, ks, vq, vs, [1, 1], sm)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            np.testing.assert_allclose(O[b, h], vq[b, g, 0].astype(np.float64) * float(vs[b, g, 0]), rtol=1e-14)
+            logit = sm * float(ks[b, g, 0]) * float(np.dot(q[b, h], kq[b, g, 0].astype(np.float64)))
+            np.testing.assert_allclose(L[b, h], logit, rtol=1e-12, atol=1e-12)
+    # two keys: softmax of two logits written out
+    O, L = dec_fn(q, kq, ks, vq, vs, [2, 2], sm)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            a = [sm * float(ks[b, g, j]) * float(q[b, h] @ kq[b, g, j]) for j in range(2)]
+            e = [math.exp(t - max(a)) for t in a]
+            want = sum(e[j] * vq[b, g, j].astype(np.float64) * float(vs[b, g, j]) for j in range(2)) / sum(e)
+            np.testing.assert_allclose(O[b, h], want, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(L[b, h], max(a) + math.log(sum(e)), rtol=1e-12, atol=1e-12)
+    # a zero query weighs every key alike: the mean of the values, LSE = ln n
+    O, L = dec_fn(np.zeros_like(q), kq, ks, vq, vs, [5, 3], sm)
+    for b, n in enumerate([5, 3]):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            want = (vq[b, g, :n].astype(np.float64) * vs[b, g, :n, None].astype(np.float64)).mean(0)
+            np.testing.assert_allclose(O[b, h], want, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(L[b, h], math.log(n), rtol=1e-14)
+    # scaling the V scales scales O; scaling the K scales by c equals a softmax scale c times larger
+    O1, L1 = dec_fn(q, kq, ks, vq, vs, [6, 4], sm)
+    O2, L2 = dec_fn(q, kq, ks, vq, (vs * 4).astype(np.float32), [6, 4], sm)
+    np.testing.assert_allclose(O2, 4 * O1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(L2, L1, rtol=0, atol=0)
+    O3, L3 = dec_fn(q, kq, (ks * 2).astype(np.float32), vq, vs, [6, 4], sm)
+    O4, L4 = dec_fn(q, kq, ks, vq, vs, [6, 4], 2 * sm)
+    np.testing.assert_allclose(O3, O4, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(L3, L4, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_int8_closed_forms():
+    _check_decode_int8(oq.decode_int8_ref)
+
+
+def test_quantized_decode_approximates_float_decode():
+    """Quantizing a bf16 cache and decoding the codes stays close to decoding the bf16 cache:
+    per-row absmax int8 keeps each value within amax/254, far below the tolerance used here."""
+    rng = np.random.default_rng(47)
+    B, Hq, Hkv, D, Lmax = 2, 8, 2, 64, 50
+    q = torch.from_numpy(rng.standard_normal((B, Hq, D))).to(torch.bfloat16)
+    kc = torch.from_numpy(rng.standard_normal((B, Hkv, Lmax, D))).to(torch.bfloat16)
+    vc = torch.from_numpy(rng.standard_normal((B, Hkv, Lmax, D))).to(torch.bfloat16)
+    kq, ks = oq.kv_quantize_ref(kc)
+    vq, vs = oq.kv_quantize_ref(vc)
+    O, L = oq.decode_int8_ref(q, kq, ks, vq, vs, [50, 31], 0.125)
+    Of, Lf = oatt.decode_ref(q, kc, vc, [50, 31], 0.125)
+    assert np.max(np.abs(O - Of)) < 2e-2 and np.max(np.abs(L - Lf)) < 2e-2
+    assert np.max(np.abs(O - Of)) > 0  # the quantization really changed the cache
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 
 def _perm_swapped_chunk_order(seq, cp):
@@ -422,6 +537,27 @@ def _merge_unweighted(o_parts, lse_parts):
     return O, L
 
 
+def _quant_half_away(x):
+    # rounds ties away from zero instead of to even
+    codes, scales = oq.kv_quantize_ref(x)
+    x32 = np.asarray(x, dtype=np.float32).reshape(-1, np.shape(x)[-1])
+    s = scales.reshape(-1)
+    out = codes.reshape(x32.shape).copy()
+    for i in range(x32.shape[0]):
+        if s[i] != 0:
+            t = x32[i] / s[i]
+            out[i] = np.clip(np.sign(t) * np.floor(np.abs(t) + np.float32(0.5)), -127, 127).astype(np.int8)
+    return out.reshape(np.shape(x)), scales
+
+
+def _dec_int8_k_scale_on_v(q, kq, ks, vq, vs, lengths, scale):
+    return oq.decode_int8_ref(q, kq, ks, vq, ks, lengths, scale)
+
+
+def _dec_int8_no_k_scale(q, kq, ks, vq, vs, lengths, scale):
+    return oq.decode_int8_ref(q, kq, np.ones_like(ks), vq, vs, lengths, scale)
+
+
 @pytest.mark.parametrize("check", [
     lambda: _check_golden(_perm_swapped_chunk_order),
     lambda: _check_balance(_perm_unbalanced, 64, 4),
@@ -431,8 +567,11 @@ def _merge_unweighted(o_parts, lse_parts):
     lambda: _check_brute(_att_transposed_v, 8, 2, 2, 1, 4, 4, 3),
     lambda: _check_decode(_dec_off_by_one),
     lambda: _check_merge(_merge_unweighted),
+    lambda: _check_quant_golden(_quant_half_away),
+    lambda: _check_decode_int8(_dec_int8_k_scale_on_v),
+    lambda: _check_decode_int8(_dec_int8_no_k_scale),
 ], ids=["chunk-order", "unbalanced", "strict-mask", "no-scale", "wrong-group", "mirrored-v", "decode-length",
-        "merge-unweighted"])
+        "merge-unweighted", "quant-ties-away", "int8-k-scale-on-v", "int8-no-k-scale"])
 def test_planted_mistakes_are_caught(check):
     with pytest.raises((AssertionError, ValueError, IndexError)):
         check()

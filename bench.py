@@ -16,7 +16,7 @@ removes (`load_balance`; skip with --no-balance-demo).
 
 Also measured: GQA decode (Mixtral-8x22B shape, batch 24, 48/8 heads, D 128, cache 2048 with
 lengths uniform in [1024, 2048]), rotating 4 cache copies so reads come from HBM rather than
-the 256 MB last-level cache; and the CPU fp64 oracle on a bounded row sample of the same
+the 256 MB last-level cache; the same decode over an int8-quantized cache (6 copies); and the CPU fp64 oracle on a bounded row sample of the same
 prefill workload (the CPU baseline).
 
 Prints one JSON line.
@@ -40,19 +40,26 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-def profiled_traffic(profile, source):
+def profiled_traffic(profile, sources):
     """HBM bytes per launch recorded in a committed rocprofv3 summary under profiles/ (FETCH_SIZE
     and WRITE_SIZE, scaled by a plain-copy calibration), or None when the summary is missing or
-    the kernel source has changed since the counters were taken (its sha256 differs)."""
+    any source file of the kernels has changed since the counters were taken: the summary lists
+    ``source_sha256[<file>] = <hex>`` for each file and every one must match."""
     import hashlib
     try:
         text = open(os.path.join(ROOT, "profiles", profile)).read()
-        src = open(os.path.join(ROOT, "context_causal_attention_load_amd", "csrc", source), "rb").read()
     except OSError:
         return None
     fields = dict(line.split(" = ", 1) for line in text.splitlines()
-                  if line.startswith(("traffic_bytes_per_launch = ", "kernel_source_sha256 = ")))
-    if fields.get("kernel_source_sha256", "").strip() != hashlib.sha256(src).hexdigest():
+                  if line.startswith(("traffic_bytes_per_launch = ", "source_sha256[")))
+    for src in sources:
+        try:
+            data = open(os.path.join(ROOT, "context_causal_attention_load_amd", "csrc", src), "rb").read()
+        except OSError:
+            return None
+        if fields.get(f"source_sha256[{src}]", "").strip() != hashlib.sha256(data).hexdigest():
+            return None
+    if "traffic_bytes_per_launch = " not in text:
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -188,6 +195,39 @@ def bench_decode(w, iters, dev, copies=4):
     return dict(median_ms=med, min_ms=ms[0], bytes=alg, gbs=alg / (med * 1e-3) / 1e9)
 
 
+def bench_decode_int8(w, iters, dev, copies=6):
+    """The same decode batch over an int8 cache (codes plus one float32 scale per cached row),
+    rotating ``copies`` caches so reads come from HBM."""
+    import context_causal_attention_load_amd as cpa
+    from context_causal_attention_load_amd import synth
+
+    lengths, q, kq, ks, vq, vs = synth.workload_decode_int8_inputs(w)
+    qd, ld = q.to(dev), lengths.to(dev)
+    caches = [tuple(t.to(dev) for t in (kq, ks, vq, vs))]
+    for _ in range(copies - 1):
+        caches.append(tuple(t.clone() for t in caches[0]))
+    ws = torch.empty(cpa.decode_workspace_bytes(w.batch, w.hq, w.hkv, w.max_len, w.d), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.batch, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.hq), dtype=torch.float32, device=dev)
+    for c in caches:
+        cpa.decode_int8(qd, c[0], c[1], c[2], c[3], ld, scale=w.scale, workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        c = caches[i % copies]
+        evs[i][0].record()
+        cpa.decode_int8(qd, c[0], c[1], c[2], c[3], ld, scale=w.scale, workspace=ws, out=out, lse=lse)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    rows = int(lengths.sum()) * w.hkv
+    kv_bytes = rows * w.d * 2 + rows * 4 * 2          # K and V codes, K and V row scales
+    io_bytes = w.batch * w.hq * w.d * 2 * 2 + w.batch * w.hq * 4 + w.batch * 4
+    alg = kv_bytes + io_bytes
+    med = ms[len(ms) // 2]
+    return dict(median_ms=med, min_ms=ms[0], bytes=alg, gbs=alg / (med * 1e-3) / 1e9)
+
+
 def cpu_baseline(w, cp, rank, n_rows, seed=0):
     """Time the CPU fp64 oracle (as it is) on a row sample of one rank: its permutes of the
     rank's windows plus attention for ``n_rows`` query rows over all heads."""
@@ -266,7 +306,8 @@ def main():
                    "ranks_timed": sorted(pre["per_rank_ms"].keys())},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": profiled_traffic("attn_fwd_bf16_llama70b_s131072_cp8.md", "attn_fwd.hip"),
+                     "traffic": profiled_traffic("attn_fwd_bf16_llama70b_s131072_cp8.md",
+                                                 ("attn_fwd.hip", "common.h")),
                      "traffic_unit": "HBM bytes per launch",
                      "kernel": "attn_fwd_bf16_kernel<128,128>", "kernel_avg_ms": round(attn_avg_ms, 4),
                      "useful_flop_per_launch": pre["flops"]},
@@ -282,9 +323,19 @@ def main():
                             "roofline": {"bound": "hbm", "achieved": round(d["gbs"], 1), "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": round(d["gbs"] / PEAK_HBM_GBS, 4),
                                          "traffic": profiled_traffic("decode_gqa_mixtral8x22b_b24_l2048.md",
-                                                                     "decode.hip"),
+                                                                     ("decode.hip", "common.h")),
                                          "traffic_unit": "HBM bytes per call (split + merge)",
                                          "algorithmic_bytes": d["bytes"]}}
+        d8 = bench_decode_int8(dw, args.decode_iters, dev)
+        result["decode_int8"] = {
+            "workload": dw.name + " with the KV cache quantized to int8 (one float32 scale per cached row)",
+            "value": round(d8["gbs"], 1), "unit": "GB/s", "median_us": round(d8["median_ms"] * 1e3, 2),
+            "min_us": round(d8["min_ms"] * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(d8["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(d8["gbs"] / PEAK_HBM_GBS, 4),
+                         "traffic": profiled_traffic("decode_int8_mixtral8x22b_b24_l2048.md",
+                                                     ("decode_int8.hip", "decode.hip", "common.h")),
+                         "traffic_unit": "HBM bytes per call (split + merge)", "algorithmic_bytes": d8["bytes"]}}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, cp, 0, args.cpu_rows)
         cb.pop("seconds")

@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     attention_fwd,
     decode,
     decode_merge,
+    decode_int8,
+    quantize_kv,
     decode_workspace_bytes,
     lb_source_index,
     lb_positions,

@@ -63,6 +63,11 @@ def load_library():
                                          vp, ctypes.c_size_t, vp]
     lib.gqa_decode_merge.restype = ctypes.c_int
     lib.gqa_decode_merge.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.gqa_decode_attention_int8kv.restype = ctypes.c_int
+    lib.gqa_decode_attention_int8kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                                vp, ctypes.c_size_t, vp]
+    lib.kv_cache_quantize_int8.restype = ctypes.c_int
+    lib.kv_cache_quantize_int8.argtypes = [vp, vp, vp, i64, i32, i32, vp]
     _lib = lib
     return lib
 
@@ -236,4 +241,64 @@ def decode_merge(o_parts, lse_parts, out=None, lse=None, want_lse=True):
     _check("gqa_decode_merge",
            load_library().gqa_decode_merge(_ptr(o_parts), _ptr(lse_parts), _ptr(out), _ptr(lse), R, B, Hq, D,
                                            _DTYPES[o_parts.dtype], _stream(o_parts.device)))
+    return out, lse
+
+
+def quantize_kv(x, codes=None, scales=None):
+    """Int8 absmax quantization of every row (last dim) of x (bf16 or fp32, GPU): one float32
+    scale per row. Returns (codes int8 of x's shape, scales float32 of x.shape[:-1])."""
+    _need_gpu(x, codes, scales)
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be float32 or bfloat16")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if codes.dtype != torch.int8 or codes.shape != x.shape:
+        raise ValueError("codes must be int8 of x's shape")
+    if scales.dtype != torch.float32 or scales.shape != x.shape[:-1]:
+        raise ValueError("scales must be float32 of x.shape[:-1]")
+    _check("kv_cache_quantize_int8",
+           load_library().kv_cache_quantize_int8(_ptr(x), _ptr(codes), _ptr(scales), rows, d, _DTYPES[x.dtype],
+                                                 _stream(x.device)))
+    return codes, scales
+
+
+def decode_int8(q, k_codes, k_scales, v_codes, v_scales, lengths, scale=None, workspace=None, out=None, lse=None,
+                want_lse=True):
+    """GQA single-token decode over an int8 cache. q [B, Hq, 128] bf16; codes int8 [B, Hkv, Lmax,
+    128]; scales float32 [B, Hkv, Lmax]; lengths int32 [B] (GPU). Returns (O [B, Hq, 128] bf16,
+    LSE [B, Hq] fp32)."""
+    _need_gpu(q, k_codes, k_scales, v_codes, v_scales, lengths, workspace, out, lse)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16")
+    if k_codes.dtype != torch.int8 or v_codes.dtype != torch.int8:
+        raise ValueError("codes must be int8")
+    if k_scales.dtype != torch.float32 or v_scales.dtype != torch.float32:
+        raise ValueError("scales must be float32")
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_codes.shape[1], k_codes.shape[2]
+    if k_codes.shape != (B, Hkv, Lmax, D) or v_codes.shape != (B, Hkv, Lmax, D):
+        raise ValueError("code cache shapes do not match q")
+    if k_scales.shape != (B, Hkv, Lmax) or v_scales.shape != (B, Hkv, Lmax):
+        raise ValueError("scales must be [B, Hkv, Lmax]")
+    if lengths.dtype != torch.int32 or lengths.shape != (B,):
+        raise ValueError("lengths must be int32 [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_workspace_bytes(B, Hq, Hkv, Lmax, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check("gqa_decode_attention_int8kv",
+           load_library().gqa_decode_attention_int8kv(_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scales),
+                                                      _ptr(v_scales), _ptr(lengths), _ptr(out), _ptr(lse), B, Hq,
+                                                      Hkv, D, Lmax, float(scale), _ptr(workspace),
+                                                      workspace.numel() * workspace.element_size(),
+                                                      _stream(q.device)))
     return out, lse

@@ -242,6 +242,75 @@ int gqa_decode_attention(const void* q, const void* k_cache, const void* v_cache
   return CPA_OK;
 }
 
+int gqa_decode_attention_int8kv(const void* q, const int8_t* k_codes, const int8_t* v_codes,
+                                const float* k_scales, const float* v_scales, const int32_t* lengths, void* o,
+                                float* lse, int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t max_len,
+                                float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* where = "gqa_decode_attention_int8kv";
+  if (batch < 0) return fail(CPA_EINVAL, "%s: batch must be >= 0", where);
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(CPA_EINVAL, "%s: hq (%d) must be a positive multiple of hkv (%d)", where, hq, hkv);
+  if (max_len < 1) return fail(CPA_EINVAL, "%s: max_len must be >= 1", where);
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(CPA_EINVAL, "%s: softmax_scale must be finite and > 0", where);
+  if (d != 128) return fail(CPA_ENOTSUP, "%s: head dim %d not supported (128)", where, d);
+  if (batch == 0) return CPA_OK;
+  const int64_t head_blocks = (int64_t)hkv * ((hq / hkv + 15) / 16);
+  if (batch > 65535 || head_blocks > 65535)
+    return fail(CPA_EINVAL, "%s: batch and hkv * ceil(G / 16) must be <= 65535", where);
+  if ((int64_t)batch * hkv * max_len * d >= (int64_t(1) << 40)) return fail(CPA_EINVAL, "%s: cache too large", where);
+  if (!q || !k_codes || !v_codes || !k_scales || !v_scales || !lengths || !o || !workspace)
+    return fail(CPA_EINVAL, "%s: null pointer", where);
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(o) || !aligned16(workspace))
+    return fail(CPA_EINVAL, "%s: q, code caches, o and workspace must be 16-byte aligned", where);
+  if (((uintptr_t)k_scales & 3u) || ((uintptr_t)v_scales & 3u) || ((uintptr_t)lengths & 3u) ||
+      (lse && ((uintptr_t)lse & 3u)))
+    return fail(CPA_EINVAL, "%s: scales, lengths and lse must be 4-byte aligned", where);
+  size_t need = gqa_decode_workspace_bytes(batch, hq, hkv, max_len, d);
+  if (workspace_bytes < need)
+    return fail(CPA_EINVAL, "%s: workspace of %zu bytes, need %zu", where, workspace_bytes, need);
+  int rc = check_device(where);
+  if (rc) return rc;
+  DecodeInt8Args a;
+  a.q = q;
+  a.k = k_codes;
+  a.v = v_codes;
+  a.k_scale = k_scales;
+  a.v_scale = v_scales;
+  a.lengths = lengths;
+  a.o = o;
+  a.lse = lse;
+  a.ws = static_cast<float*>(workspace);
+  a.batch = batch;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.max_len = max_len;
+  a.scale = softmax_scale;
+  hipError_t e = launch_decode_int8(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, where);
+  return CPA_OK;
+}
+
+int kv_cache_quantize_int8(const void* x, int8_t* codes, float* scales, int64_t rows, int32_t d, int32_t dtype,
+                           void* stream) {
+  const char* where = "kv_cache_quantize_int8";
+  if (rows < 0) return fail(CPA_EINVAL, "%s: rows must be >= 0", where);
+  if (d < 1) return fail(CPA_EINVAL, "%s: d must be >= 1", where);
+  if (dtype != CPA_F32 && dtype != CPA_BF16) return fail(CPA_EINVAL, "%s: unknown dtype %d", where, dtype);
+  if (rows == 0) return CPA_OK;
+  if (rows >= (int64_t(1) << 33) || rows * d >= (int64_t(1) << 40))
+    return fail(CPA_EINVAL, "%s: rows * d too large", where);
+  if (!x || !codes || !scales) return fail(CPA_EINVAL, "%s: null pointer", where);
+  const uintptr_t elem = dtype == CPA_BF16 ? 1u : 3u;
+  if (((uintptr_t)x & elem) || ((uintptr_t)scales & 3u))
+    return fail(CPA_EINVAL, "%s: x and scales must be aligned to their element size", where);
+  int rc = check_device(where);
+  if (rc) return rc;
+  hipError_t e = launch_kv_quantize(x, codes, scales, rows, d, dtype == CPA_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, where);
+  return CPA_OK;
+}
+
 int gqa_decode_merge(const void* o_parts, const float* lse_parts, void* o, float* lse, int32_t parts,
                      int32_t batch, int32_t hq, int32_t d, int32_t dtype, void* stream) {
   const char* where = "gqa_decode_merge";

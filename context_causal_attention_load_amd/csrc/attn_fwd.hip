@@ -88,29 +88,6 @@ __device__ __forceinline__ int wave_max_i(int x) {
 }
 
 
-// 16-byte global -> LDS copy per lane (gfx950 global_load_lds_dwordx4): lane l's bytes land at
-// LDS address lds_wave_base + 16*l. Issued through inline asm so that the compiler does not
-// make the reads of the other LDS stage wait for it; the caller waits (vmcnt) before the barrier
-// that publishes the stage.
-__device__ __forceinline__ void dma16(const void* gptr, const char* lds_wave_base) {
-  const unsigned lds_addr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
-}
-
-// The same copy from a wave-uniform base plus a per-lane 32-bit byte offset (the base lives in
-// scalar registers, so a tile's copies need no per-lane 64-bit address arithmetic).
-__device__ __forceinline__ void dma16_sv(const char* base, unsigned voff, unsigned lds_wave_addr) {
-  // readfirstlane yields int: both halves go through unsigned so that the low word is
-  // zero-extended (a sign-extended low word would corrupt the high word of the address)
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
-  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
-  const char* sbase = reinterpret_cast<const char*>((hi << 32) | lo);
-  const unsigned lds_addr = __builtin_amdgcn_readfirstlane(lds_wave_addr);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
-               : "memory", "m0");
-}
-
 struct WorkItem {
   int b, g, head0, row_blk;
 };

@@ -31,6 +31,23 @@ __host__ __device__ inline int64_t lb_chunk_offset(int64_t i, int64_t c, int64_t
   return i < cp ? i * 2 * c : (2 * cp - 1 - i) * 2 * c + c;
 }
 
+// 16-byte global -> LDS copy per lane (gfx950 global_load_lds_dwordx4) from a wave-uniform base
+// plus a per-lane 32-bit byte offset: lane l's 16 bytes land at LDS address lds_wave_addr + 16*l.
+// Issued through inline asm, so the compiler neither tracks nor waits for it: the caller waits
+// (s_waitcnt vmcnt) before the LDS bytes are read. The base lives in scalar registers, so a
+// tile's copies need no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16_sv(const char* base, unsigned voff, unsigned lds_wave_addr) {
+  // readfirstlane yields int: both halves go through unsigned so that the low word is
+  // zero-extended (a sign-extended low word would corrupt the high word of the address)
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
+  const char* sbase = reinterpret_cast<const char*>((hi << 32) | lo);
+  const unsigned lds_addr = __builtin_amdgcn_readfirstlane(lds_wave_addr);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // Number of XCDs on MI355X: consecutive workgroup ids are dealt round-robin to them, and each
 // has its own L2.
 constexpr int kNumXcd = 8;
@@ -76,6 +93,26 @@ struct DecodeMergeArgs {
   bool bf16;
 };
 hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream);
+
+struct DecodeInt8Args {
+  const void* q;          // bf16 [batch, hq, 128]
+  const int8_t* k;        // [batch, hkv, max_len, 128] codes
+  const int8_t* v;
+  const float* k_scale;   // [batch, hkv, max_len] one scale per cached row
+  const float* v_scale;
+  const int32_t* lengths;
+  void* o;                // bf16 [batch, hq, 128]
+  float* lse;             // may be null
+  float* ws;              // split partials, as for DecodeArgs
+  int batch, hq, hkv, max_len;
+  float scale;
+};
+hipError_t launch_decode_int8(const DecodeInt8Args& a, hipStream_t stream);
+hipError_t launch_kv_quantize(const void* x, int8_t* codes, float* scales, int64_t rows, int d, bool bf16,
+                              hipStream_t stream);
+// Second decode pass alone: merges the split partials in ws into o (bf16 or fp32) and lse.
+hipError_t launch_decode_split_merge(const int32_t* lengths, float* ws, void* o, float* lse, int batch, int hq,
+                                     int max_len, int d, bool bf16, hipStream_t stream);
 
 // Decode split geometry, shared by the workspace-size query and the launcher. The workspace
 // holds the split partials [batch, hq, nsplit, d + 2] in float32: d unnormalised outputs, then

@@ -543,6 +543,36 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch_typed<__bf16>(a, stream); }
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) { return launch_typed<float>(a, stream); }
 
+hipError_t launch_decode_split_merge(const int32_t* lengths, float* ws, void* o, float* lse, int batch, int hq,
+                                     int max_len, int d, bool bf16, hipStream_t stream) {
+  if (batch == 0 || hq == 0) return hipSuccess;
+  DecParams p{};
+  p.lengths = lengths;
+  p.ws = ws;
+  p.o = o;
+  p.lse = lse;
+  p.B = batch;
+  p.Hq = hq;
+  p.max_len = max_len;
+  p.nsplit = decode_nsplit(max_len);
+  p.split_len = kDecodeSplitLen;
+  const dim3 grid((unsigned)((int64_t)batch * hq));
+  if (d == 128) {
+    if (bf16)
+      hipLaunchKernelGGL((decode_merge_kernel<__bf16, 128>), grid, dim3(128), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<float, 128>), grid, dim3(128), 0, stream, p);
+  } else if (d == 64) {
+    if (bf16)
+      hipLaunchKernelGGL((decode_merge_kernel<__bf16, 64>), grid, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<float, 64>), grid, dim3(64), 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream) {
   const int64_t bh = (int64_t)a.batch * a.hq;
   if (bh == 0) return hipSuccess;

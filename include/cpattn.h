@@ -174,6 +174,41 @@ int gqa_decode_attention(const void* q, const void* k_cache, const void* v_cache
 int gqa_decode_merge(const void* o_parts, const float* lse_parts, void* o, float* lse, int32_t parts,
                      int32_t batch, int32_t hq, int32_t d, int32_t dtype, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * int8 KV cache ("rename context to context_autoregressive", PR 1453, Description: the decode
+ * benchmark runs with the KV cache quantized to int8). The page names the setting, not its
+ * arithmetic; the reading implemented is symmetric absmax quantization with one float32 scale per
+ * cached row (sequence, kv head, position):
+ *   amax = max_d |x_d|,  scale = amax / 127,  code_d = round_half_even(x_d / scale) in [-127, 127],
+ * with both divisions correctly rounded in float32; a row of zeros gets scale 0 and codes 0.
+ *
+ * kv_cache_quantize_int8: quantizes `rows` rows of `d` values.
+ *   x       [rows, d] in dtype (CPA_BF16 or CPA_F32, device), finite values
+ *   codes   [rows, d] int8 (device, output); scales [rows] float32 (device, output)
+ * CPA_EINVAL for negative rows, d < 1, an unknown dtype, a null pointer or x / scales not aligned
+ * to their element size. rows == 0 returns CPA_OK without touching the device. */
+int kv_cache_quantize_int8(const void* x, int8_t* codes, float* scales, int64_t rows, int32_t d,
+                           int32_t dtype, void* stream);
+
+/* gqa_decode_attention_int8kv: gqa_decode_attention over a quantized cache; K and V are read as
+ * code * scale, everything else (lengths, GQA grouping, outputs, workspace) is as there.
+ *   q        [B, Hq, 128] bf16 (device)
+ *   k_codes, v_codes   [B, Hkv, max_len, 128] int8 (device, 16-byte aligned)
+ *   k_scales, v_scales [B, Hkv, max_len] float32 (device), the per-row scales
+ *   lengths  [B] int32 (device), 0 <= lengths[b] <= max_len; entries at or past a length are not
+ *            used (they may hold anything); a length of 0 gives O = 0 and LSE = -inf
+ *   o        [B, Hq, 128] bf16 (output); lse [B, Hq] float32 (output, may be NULL)
+ *   workspace, workspace_bytes: at least gqa_decode_workspace_bytes(B, Hq, Hkv, max_len, 128)
+ *            bytes of caller-owned device scratch; calls sharing one workspace must not overlap.
+ * Supported: head dim 128, B <= 65535, Hkv * ceil((Hq / Hkv) / 16) <= 65535. CPA_ENOTSUP for other
+ * head dims; CPA_EINVAL for bad sizes, null or misaligned pointers, a small workspace or a
+ * non-positive scale. */
+int gqa_decode_attention_int8kv(const void* q, const int8_t* k_codes, const int8_t* v_codes,
+                                const float* k_scales, const float* v_scales, const int32_t* lengths,
+                                void* o, float* lse, int32_t batch, int32_t hq, int32_t hkv, int32_t d,
+                                int32_t max_len, float softmax_scale, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("cp_load_balance_permute", "cp_load_balance_unpermute", "cp_attention_fwd",
                  "gqa_decode_attention", "gqa_decode_workspace_bytes", "cpattn_last_error",
-                 "cp_load_balance_source_index", "cp_load_balance_positions"):
+                 "cp_load_balance_source_index", "cp_load_balance_positions", "gqa_decode_merge",
+                 "gqa_decode_attention_int8kv", "kv_cache_quantize_int8"):
         assert must in names, names
 
 
@@ -178,6 +179,63 @@ def test_decode_merge_argument_errors(lib, kw, status, substr):
 def test_decode_merge_empty_is_ok_without_device(lib):
     assert _merge(lib, batch=0)[0] == 0
     assert _merge(lib, hq=0)[0] == 0
+
+
+def _dec8(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, lengths=FAKE, o=FAKE, lse=None, batch=24, hq=48, hkv=8, d=128,
+             max_len=2048, scale=0.088, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    rc = lib.gqa_decode_attention_int8kv(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["lengths"], a["o"], a["lse"],
+                                         a["batch"], a["hq"], a["hkv"], a["d"], a["max_len"], a["scale"], a["ws"],
+                                         a["ws_bytes"], None)
+    return _status_and_message(lib, rc)
+
+
+@pytest.mark.parametrize("kw,status,substr", [
+    (dict(hq=50), binding.CPA_EINVAL, "multiple of hkv"),
+    (dict(batch=-1), binding.CPA_EINVAL, "batch"),
+    (dict(max_len=0), binding.CPA_EINVAL, "max_len"),
+    (dict(scale=float("inf")), binding.CPA_EINVAL, "softmax_scale"),
+    (dict(d=64), binding.CPA_ENOTSUP, "head dim"),
+    (dict(batch=70000), binding.CPA_EINVAL, "65535"),
+    (dict(ks=None), binding.CPA_EINVAL, "null"),
+    (dict(ws_bytes=1024), binding.CPA_EINVAL, "workspace"),
+    (dict(k=ctypes.c_void_p(4104)), binding.CPA_EINVAL, "aligned"),
+    (dict(vs=ctypes.c_void_p(4098)), binding.CPA_EINVAL, "aligned"),
+])
+def test_decode_int8_argument_errors(lib, kw, status, substr):
+    rc, msg = _dec8(lib, **kw)
+    assert rc == status and substr in msg, (rc, msg)
+
+
+def test_decode_int8_empty_is_ok_without_device(lib):
+    assert _dec8(lib, batch=0)[0] == 0
+
+
+def _quant(lib, **kw):
+    a = dict(x=FAKE, codes=FAKE, scales=FAKE, rows=100, d=128, dtype=binding.CPA_BF16)
+    a.update(kw)
+    rc = lib.kv_cache_quantize_int8(a["x"], a["codes"], a["scales"], a["rows"], a["d"], a["dtype"], None)
+    return _status_and_message(lib, rc)
+
+
+@pytest.mark.parametrize("kw,status,substr", [
+    (dict(rows=-1), binding.CPA_EINVAL, "rows"),
+    (dict(d=0), binding.CPA_EINVAL, "d must"),
+    (dict(dtype=9), binding.CPA_EINVAL, "dtype"),
+    (dict(codes=None), binding.CPA_EINVAL, "null"),
+    (dict(x=ctypes.c_void_p(4097)), binding.CPA_EINVAL, "aligned"),
+    (dict(x=ctypes.c_void_p(4098), dtype=binding.CPA_F32), binding.CPA_EINVAL, "aligned"),
+    (dict(scales=ctypes.c_void_p(4102)), binding.CPA_EINVAL, "aligned"),
+    (dict(rows=1 << 34), binding.CPA_EINVAL, "too large"),
+])
+def test_quantize_argument_errors(lib, kw, status, substr):
+    rc, msg = _quant(lib, **kw)
+    assert rc == status and substr in msg, (rc, msg)
+
+
+def test_quantize_empty_is_ok_without_device(lib):
+    assert _quant(lib, rows=0)[0] == 0
 
 
 def test_decode_workspace_size(lib):

@@ -403,3 +403,117 @@ def test_decode_workspace_reuse():
         O_ref, L_ref = oatt.decode_ref(q, kc, vc, lengths.numpy(), 1.0 / math.sqrt(d))
         assert_close(o.float().cpu().numpy(), O_ref, 2e-2, f"decode O call {it}")
         assert_close(lse.cpu().numpy(), L_ref, 2e-2, f"decode LSE call {it}")
+
+
+# ----------------------------------------------------------------------------- int8 cache
+
+from oracle import quant as oq  # noqa: E402
+
+
+@pytest.mark.parametrize("rows,d,dtype", [
+    (24 * 8 * 64, 128, torch.bfloat16),   # 64 cache positions of the Mixtral-shaped cache
+    (1000, 128, torch.float32),
+    (37, 64, torch.bfloat16),
+    (5, 100, torch.float32),              # a row length that is not a multiple of the wave
+    (3, 1, torch.bfloat16),
+])
+def test_quantize_bit_exact(rows, d, dtype):
+    """Codes and scales of the HIP quantizer equal the oracle's bit for bit (both take every
+    rounding decision in float32). Includes zero rows, rows with one large outlier and a row whose
+    absmax is negative."""
+    announce(f"kv quantize rows={rows} d={d} {dtype}")
+    gen = torch.Generator("cpu").manual_seed(rows + d)
+    x = (torch.randn((rows, d), generator=gen) * torch.rand((rows, 1), generator=gen) * 8).to(dtype)
+    x[0] = 0
+    if rows > 2:
+        x[1, d // 2] = -1000.0
+        x[2] = x[2].abs()
+        x[2, 0] = -3 * x[2].abs().max()
+    codes, scales = cpa.quantize_kv(x.to(DEV))
+    torch.cuda.synchronize()
+    c_ref, s_ref = oq.kv_quantize_ref(x)
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    bad = int((got_c != c_ref).sum())
+    print(f"  code mismatches {bad}, scale mismatches {int((got_s != s_ref).sum())}", flush=True)
+    assert bad == 0
+    assert np.array_equal(got_s.view(np.uint32), s_ref.view(np.uint32))
+
+
+def run_decode_int8(lengths, q, kq, ks, vq, vs, scale, workspace=None):
+    o, lse = cpa.decode_int8(q.to(DEV), kq.to(DEV), ks.to(DEV), vq.to(DEV), vs.to(DEV), lengths.to(DEV),
+                             scale=scale, workspace=workspace)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def test_decode_int8_full_workload_with_poisoned_tail():
+    """Mixtral-8x22B-shaped decode batch over an int8 cache; scales past each length are NaN and
+    codes there are -128 (a value the quantizer never writes): neither may leak into the result."""
+    w = synth.MIXTRAL_8X22B_DECODE
+    announce(f"int8 decode {w.name} (poisoned beyond each length)")
+    lengths, q, kq, ks, vq, vs = synth.workload_decode_int8_inputs(w)
+    O_ref, L_ref = oq.decode_int8_ref(q, kq, ks, vq, vs, lengths.numpy(), w.scale)
+    for b in range(w.batch):
+        n = int(lengths[b])
+        ks[b, :, n:] = float("nan")
+        vs[b, :, n:] = float("nan")
+        kq[b, :, n:] = -128
+        vq[b, :, n:] = -128
+    o, lse = run_decode_int8(lengths, q, kq, ks, vq, vs, w.scale)
+    assert_close(o, O_ref, 2e-2, "int8 decode O")
+    assert_close(lse, L_ref, 2e-2, "int8 decode LSE")
+
+
+@pytest.mark.parametrize("batch,hq,hkv,max_len,lens", [
+    (4, 48, 8, 2048, [1, 2048, 256, 257]),
+    (3, 16, 1, 300, [300, 1, 255]),          # G = 16: one full head block
+    (2, 40, 2, 513, [513, 17]),              # G = 20: two head blocks, the second partial
+    (2, 64, 2, 130, [64, 130]),              # G = 32
+    (5, 12, 4, 1000, [999, 1000, 512, 3, 768]),
+    (2, 1, 1, 1, [1, 1]),                    # one key, one head
+])
+def test_decode_int8_edge_lengths(batch, hq, hkv, max_len, lens):
+    announce(f"int8 decode B={batch} Hq={hq} Hkv={hkv} Lmax={max_len} lens={lens}")
+    lengths, q, kq, ks, vq, vs = synth.decode_int8_inputs(batch, hq, hkv, 128, max_len, 1, max_len,
+                                                          seed=batch + hq + max_len)
+    lengths = torch.tensor(lens, dtype=torch.int32)
+    scale = 1.0 / math.sqrt(128)
+    O_ref, L_ref = oq.decode_int8_ref(q, kq, ks, vq, vs, lengths.numpy(), scale)
+    for b in range(batch):
+        ks[b, :, lens[b]:] = float("nan")
+        vs[b, :, lens[b]:] = float("nan")
+    o, lse = run_decode_int8(lengths, q, kq, ks, vq, vs, scale)
+    assert_close(o, O_ref, 2e-2, "int8 decode O")
+    assert_close(lse, L_ref, 2e-2, "int8 decode LSE")
+
+
+def test_decode_int8_zero_length_and_workspace_reuse():
+    """Length 0 gives O = 0, LSE = -inf; a garbage-filled workspace serves two calls in a row,
+    the second with a smaller batch."""
+    announce("int8 decode: zero length, workspace reuse")
+    B, hq, hkv, lmax = 4, 24, 4, 700
+    ws = torch.full((cpa.decode_workspace_bytes(B, hq, hkv, lmax, 128),), 0x7F, dtype=torch.uint8, device=DEV)
+    for it, (b, seed) in enumerate([(4, 51), (2, 52)]):
+        lengths, q, kq, ks, vq, vs = synth.decode_int8_inputs(b, hq, hkv, 128, lmax, 1, lmax, seed=seed)
+        lengths[0] = 0
+        o, lse = run_decode_int8(lengths, q, kq, ks, vq, vs, 1.0 / math.sqrt(128), workspace=ws)
+        assert np.all(o[0] == 0.0) and np.all(lse[0] == -np.inf)
+        O_ref, L_ref = oq.decode_int8_ref(q, kq, ks, vq, vs, lengths.numpy(), 1.0 / math.sqrt(128))
+        assert_close(o[1:], O_ref[1:], 2e-2, f"int8 decode O call {it}")
+        assert_close(lse[1:], L_ref[1:], 2e-2, f"int8 decode LSE call {it}")
+
+
+def test_quantize_then_decode_int8():
+    """The cache-writer path: a bf16 cache quantized on the GPU and decoded from its codes, against
+    the oracle's own quantization and decode of the same bf16 cache."""
+    announce("quantize bf16 cache then int8 decode")
+    lengths, q, kc, vc = synth.decode_inputs(6, 48, 8, 128, 1100, 1, 1100, torch.bfloat16, seed=61)
+    kq, ks = cpa.quantize_kv(kc.to(DEV))
+    vq, vs = cpa.quantize_kv(vc.to(DEV))
+    o, lse = cpa.decode_int8(q.to(DEV), kq, ks, vq, vs, lengths.to(DEV))
+    torch.cuda.synchronize()
+    kq_r, ks_r = oq.kv_quantize_ref(kc)
+    vq_r, vs_r = oq.kv_quantize_ref(vc)
+    O_ref, L_ref = oq.decode_int8_ref(q, kq_r, ks_r, vq_r, vs_r, lengths.numpy(), 1.0 / math.sqrt(128))
+    assert_close(o.float().cpu().numpy(), O_ref, 2e-2, "quantize + int8 decode O")
+    assert_close(lse.cpu().numpy(), L_ref, 2e-2, "quantize + int8 decode LSE")

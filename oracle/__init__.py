@@ -21,6 +21,8 @@ Sources (web pages, cited by title and section):
   context parallelism splits the cache along its length (merge of per-slice decodes), and the
   decode benchmark quantizes the KV cache to int8 (``oracle.quant``: the absmax per-row
   reading taken for it).
+* "Add context parallelism" (MaxText PR 1445), Description, again for the backward pass
+  (``oracle.backward``): the shard's gradients by the chain rule through the forward above.
 
 Every function computes in float64 from inputs upcast exactly from their stored dtype.
 
@@ -46,6 +48,7 @@ from .attention import (
     unpermute_ref,
 )
 from .quant import kv_quantize_ref, dequantize_ref, decode_int8_ref
+from .backward import causal_attention_bwd_ref, cp_attention_bwd_ref
 
 __all__ = [
     "load_balance_perm",
@@ -61,6 +64,8 @@ __all__ = [
     "kv_quantize_ref",
     "dequantize_ref",
     "decode_int8_ref",
+    "causal_attention_bwd_ref",
+    "cp_attention_bwd_ref",
     "permute_ref",
     "unpermute_ref",
 ]

@@ -17,6 +17,7 @@ import oracle
 from oracle import attention as oatt
 from oracle import lb_index as olb
 from oracle import quant as oq
+from oracle import backward as obw
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -482,6 +483,126 @@ def test_quantized_decode_approximates_float_decode():
     assert np.max(np.abs(O - Of)) > 0  # the quantization really changed the cache
 
 
+# ----------------------------------------------------------------------------- backward pins
+
+def _sdpa_grads(q, k, v, do, q_pos, k_pos, scale):
+    """torch float64 autograd through the library's masked scaled_dot_product_attention."""
+    B, Sq, Hq, _ = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    tq = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    tk = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    tv = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    mask = torch.as_tensor(np.asarray(k_pos))[None, :] <= torch.as_tensor(np.asarray(q_pos))[:, None]
+    kk = tk.repeat_interleave(G, dim=2).transpose(1, 2)
+    vv = tv.repeat_interleave(G, dim=2).transpose(1, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(tq.transpose(1, 2), kk, vv, attn_mask=mask, scale=scale)
+    o.backward(torch.tensor(do, dtype=torch.float64).transpose(1, 2))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def _check_bwd_library(bwd_fn, seq, cp, hq, hkv, dqk, dv, seed, batch=1):
+    """Each rank's dQ equals the library autograd dQ at its rows; the ranks' dK and dV summed
+    equal the library's (keys compared in gathered order)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((batch, seq, hq, dqk))
+    k = rng.standard_normal((batch, seq, hkv, dqk))
+    v = rng.standard_normal((batch, seq, hkv, dv))
+    do = rng.standard_normal((batch, seq, hq, dv))
+    scale = 1.0 / math.sqrt(dqk)
+    pos = np.arange(seq)
+    dq_ref, dk_ref, dv_ref = _sdpa_grads(q, k, v, do, pos, pos, scale)
+    perm = olb.load_balance_perm(seq, cp)
+    dk_sum = np.zeros_like(k)
+    dv_sum = np.zeros_like(v)
+    for r in range(cp):
+        b0, b1 = olb.shard_row_range(seq, cp, r)
+        rows = perm[b0:b1]
+        dq, dk, dv_ = bwd_fn(q[:, rows], k[:, perm], v[:, perm], do[:, rows], rows, perm, scale)
+        np.testing.assert_allclose(dq, dq_ref[:, rows], rtol=0, atol=1e-10)
+        dk_sum += dk
+        dv_sum += dv_
+    np.testing.assert_allclose(dk_sum, dk_ref[:, perm], rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dv_sum, dv_ref[:, perm], rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("seq,cp,hq,hkv,dqk,dv,batch", [
+    (16, 1, 2, 2, 8, 8, 1),
+    (32, 2, 4, 2, 8, 4, 2),
+    (64, 4, 6, 3, 12, 8, 1),
+])
+def test_backward_matches_library_autograd(seq, cp, hq, hkv, dqk, dv, batch):
+    _check_bwd_library(obw.causal_attention_bwd_ref, seq, cp, hq, hkv, dqk, dv, 71, batch)
+
+
+def _forward_loss(q, k, v, do, q_pos, k_pos, scale):
+    o, _ = oatt.causal_attention_ref(q, k, v, q_pos, k_pos, scale)
+    return float((o * do).sum())
+
+
+def _check_bwd_finite_differences(bwd_fn):
+    """Central differences of L = sum(dO * O) through the forward oracle."""
+    rng = np.random.default_rng(73)
+    seq, cp = 8, 2
+    q = rng.standard_normal((1, 4, 2, 4))
+    k = rng.standard_normal((1, seq, 1, 4))
+    v = rng.standard_normal((1, seq, 1, 3))
+    do = rng.standard_normal((1, 4, 2, 3))
+    perm = olb.load_balance_perm(seq, cp)
+    rows = perm[4:8]
+    scale = 0.7
+    dq, dk, dv = bwd_fn(q, k, v, do, rows, perm, scale)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [tuple(int(rng.integers(0, n)) for n in x.shape) for _ in range(6)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _forward_loss(args["q"], args["k"], args["v"], do, rows, perm, scale)
+            args[name] = xm
+            lm = _forward_loss(args["q"], args["k"], args["v"], do, rows, perm, scale)
+            num = (lp - lm) / (2 * h)
+            assert abs(num - g[idx]) <= 1e-7 * max(1.0, abs(num)), (name, idx, num, g[idx])
+
+
+def test_backward_finite_differences():
+    _check_bwd_finite_differences(obw.causal_attention_bwd_ref)
+
+
+def _check_bwd_closed_forms(bwd_fn):
+    rng = np.random.default_rng(79)
+    seq, hq, hkv, d = 12, 4, 2, 6
+    pos = np.arange(seq)
+    q = rng.standard_normal((1, seq, hq, d))
+    k = rng.standard_normal((1, seq, hkv, d))
+    do = rng.standard_normal((1, seq, hq, d))
+    # constant V: O does not depend on the scores, so dQ = dK = 0 and dV_j = sum_i P_ij dO_i
+    v = np.broadcast_to(rng.standard_normal((1, 1, hkv, d)), (1, seq, hkv, d)).copy()
+    dq, dk, dv = bwd_fn(q, k, v, do, pos, pos, 0.5)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+    # identical keys: every visible key has P_ij = 1 / (i + 1), so
+    # dV_j = sum over query heads of the group and rows i >= j of dO_i / (i + 1)
+    k_same = np.broadcast_to(k[:, :1], k.shape).copy()
+    v2 = rng.standard_normal((1, seq, hkv, d))
+    dq, dk, dv = bwd_fn(q, k_same, v2, do, pos, pos, 0.5)
+    G = hq // hkv
+    for g in range(hkv):
+        for j in range(seq):
+            want = sum(do[0, i, h] / (i + 1) for i in range(j, seq) for h in range(g * G, (g + 1) * G))
+            np.testing.assert_allclose(dv[0, j, g], want, rtol=1e-12, atol=1e-12)
+    # any inputs: the softmax gradient sums to zero over each row, so dK summed over keys is 0
+    v3 = rng.standard_normal((1, seq, hkv, d))
+    dq, dk, dv = bwd_fn(q, k, v3, do, pos, pos, 0.5)
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    assert np.abs(dk).max() > 1e-3
+
+
+def test_backward_closed_forms():
+    _check_bwd_closed_forms(obw.causal_attention_bwd_ref)
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 
 def _perm_swapped_chunk_order(seq, cp):
@@ -558,6 +679,47 @@ def _dec_int8_no_k_scale(q, kq, ks, vq, vs, lengths, scale):
     return oq.decode_int8_ref(q, kq, np.ones_like(ks), vq, vs, lengths, scale)
 
 
+def _bwd_no_delta(q, k, v, do, q_pos, k_pos, scale):
+    # drops the D_i term of dS: dS = P * dP
+    k_pos = np.asarray(k_pos)
+    q_pos = np.asarray(q_pos)
+    q64, k64, v64, do64 = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    B, Sq, Hq, _ = q64.shape
+    Hkv = k64.shape[2]
+    G = Hq // Hkv
+    dq, dk, dv = np.zeros_like(q64), np.zeros_like(k64), np.zeros_like(v64)
+    vis = k_pos[None, :] <= q_pos[:, None]
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s_ = np.where(vis, scale * q64[b, :, h] @ k64[b, :, g].T, -np.inf)
+            p = np.exp(s_ - s_.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            ds = p * (do64[b, :, h] @ v64[b, :, g].T)
+            dq[b, :, h] = scale * ds @ k64[b, :, g]
+            dk[b, :, g] += scale * ds.T @ q64[b, :, h]
+            dv[b, :, g] += p.T @ do64[b, :, h]
+    return dq, dk, dv
+
+
+def _bwd_dk_unscaled(q, k, v, do, q_pos, k_pos, scale):
+    dq, dk, dv = obw.causal_attention_bwd_ref(q, k, v, do, q_pos, k_pos, scale)
+    return dq, dk / scale, dv
+
+
+def _bwd_dv_one_head(q, k, v, do, q_pos, k_pos, scale):
+    # keeps only the first query head of each group in dV
+    q = np.asarray(q, dtype=np.float64).copy()
+    dq, dk, dv = obw.causal_attention_bwd_ref(q, k, v, do, q_pos, k_pos, scale)
+    G = q.shape[2] // np.asarray(k).shape[2]
+    do0 = np.asarray(do, dtype=np.float64).copy()
+    for h in range(q.shape[2]):
+        if h % G:
+            do0[:, :, h] = 0
+    _, _, dv0 = obw.causal_attention_bwd_ref(q, k, v, do0, q_pos, k_pos, scale)
+    return dq, dk, dv0
+
+
 @pytest.mark.parametrize("check", [
     lambda: _check_golden(_perm_swapped_chunk_order),
     lambda: _check_balance(_perm_unbalanced, 64, 4),
@@ -570,8 +732,12 @@ def _dec_int8_no_k_scale(q, kq, ks, vq, vs, lengths, scale):
     lambda: _check_quant_golden(_quant_half_away),
     lambda: _check_decode_int8(_dec_int8_k_scale_on_v),
     lambda: _check_decode_int8(_dec_int8_no_k_scale),
+    lambda: _check_bwd_library(_bwd_no_delta, 32, 2, 4, 2, 8, 4, 5),
+    lambda: _check_bwd_finite_differences(_bwd_dk_unscaled),
+    lambda: _check_bwd_library(_bwd_dv_one_head, 32, 2, 4, 2, 8, 4, 5),
 ], ids=["chunk-order", "unbalanced", "strict-mask", "no-scale", "wrong-group", "mirrored-v", "decode-length",
-        "merge-unweighted", "quant-ties-away", "int8-k-scale-on-v", "int8-no-k-scale"])
+        "merge-unweighted", "quant-ties-away", "int8-k-scale-on-v", "int8-no-k-scale", "bwd-no-delta", "bwd-dk-unscaled",
+        "bwd-dv-one-head"])
 def test_planted_mistakes_are_caught(check):
     with pytest.raises((AssertionError, ValueError, IndexError)):
         check()

@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     permute,
     unpermute,
     attention_fwd,
+    attention_bwd,
+    attention_bwd_workspace_bytes,
     decode,
     decode_merge,
     decode_int8,

@@ -66,6 +66,11 @@ def load_library():
     lib.gqa_decode_attention_int8kv.restype = ctypes.c_int
     lib.gqa_decode_attention_int8kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                                 vp, ctypes.c_size_t, vp]
+    lib.cp_attention_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.cp_attention_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.cp_attention_bwd.restype = ctypes.c_int
+    lib.cp_attention_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                     i32, f32, i32, i32, vp, ctypes.c_size_t, vp]
     lib.kv_cache_quantize_int8.restype = ctypes.c_int
     lib.kv_cache_quantize_int8.argtypes = [vp, vp, vp, i64, i32, i32, vp]
     _lib = lib
@@ -302,3 +307,46 @@ def decode_int8(q, k_codes, k_scales, v_codes, v_scales, lengths, scale=None, wo
                                                       workspace.numel() * workspace.element_size(),
                                                       _stream(q.device)))
     return out, lse
+
+
+def attention_bwd_workspace_bytes(batch, sq, hq):
+    return int(load_library().cp_attention_bwd_workspace_bytes(batch, sq, hq))
+
+
+def attention_bwd(q_shard, k, v, o, lse, d_o, cp, rank, q_positions=None, scale=None, workspace=None, dq=None,
+                  dk=None, dv=None):
+    """Backward of attention_fwd for one rank (bf16). Inputs as for attention_fwd plus its O and
+    LSE and dO [B, Sq, Hq, Dv]. Returns float32 (dQ [B, Sq, Hq, Dqk], dK [B, S, Hkv, Dqk],
+    dV [B, S, Hkv, Dv]), dK/dV in the gathered key order and holding this rank's share."""
+    _need_gpu(q_shard, k, v, o, lse, d_o, q_positions, workspace, dq, dk, dv)
+    if q_shard.dtype != torch.bfloat16 or k.dtype != q_shard.dtype or v.dtype != q_shard.dtype:
+        raise ValueError("q, k and v must be bfloat16")
+    if o.dtype != q_shard.dtype or d_o.dtype != q_shard.dtype:
+        raise ValueError("o and d_o must have q's dtype")
+    B, Sq, Hq, Dqk = q_shard.shape
+    S, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if k.shape != (B, S, Hkv, Dqk) or v.shape[:3] != (B, S, Hkv):
+        raise ValueError("k and v shapes do not match q")
+    if o.shape != (B, Sq, Hq, Dv) or d_o.shape != (B, Sq, Hq, Dv):
+        raise ValueError("o and d_o must be [B, Sq, Hq, Dv]")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, Sq):
+        raise ValueError("lse must be float32 [B, Hq, Sq]")
+    if q_positions is not None and (q_positions.dtype != torch.int32 or q_positions.shape != (Sq,)):
+        raise ValueError("q_positions must be int32 [Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    dev = q_shard.device
+    if workspace is None:
+        workspace = torch.empty(max(attention_bwd_workspace_bytes(B, Sq, Hq), 16), dtype=torch.uint8, device=dev)
+    if dq is None:
+        dq = torch.empty((B, Sq, Hq, Dqk), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((B, S, Hkv, Dqk), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty((B, S, Hkv, Dv), dtype=torch.float32, device=dev)
+    _check("cp_attention_bwd",
+           load_library().cp_attention_bwd(_ptr(q_shard), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o),
+                                           _ptr(q_positions), _ptr(dq), _ptr(dk), _ptr(dv), B, S, Sq, Hq, Hkv, Dqk,
+                                           Dv, _DTYPES[q_shard.dtype], float(scale), cp, rank, _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(dev)))
+    return dq, dk, dv

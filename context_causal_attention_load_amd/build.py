@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libcpattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "permute.hip", "attn_fwd.hip", "decode.hip", "decode_int8.hip"]
+SOURCES = ["api.cpp", "permute.hip", "attn_fwd.hip", "decode.hip", "decode_int8.hip", "attn_bwd.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code; the compiler would otherwise form them
 # from ordinary float code.

@@ -189,6 +189,74 @@ int cp_attention_fwd(const void* q_shard, const void* k, const void* v, const in
   return CPA_OK;
 }
 
+size_t cp_attention_bwd_workspace_bytes(int32_t batch, int32_t sq, int32_t hq) {
+  if (batch <= 0 || sq <= 0 || hq <= 0) return 0;
+  return attn_bwd_workspace_bytes(batch, sq, hq);
+}
+
+int cp_attention_bwd(const void* q_shard, const void* k, const void* v, const void* o, const float* lse,
+                     const void* d_o, const int32_t* q_positions, float* dq, float* dk, float* dv, int32_t batch,
+                     int32_t seq, int32_t sq, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int32_t dtype,
+                     float softmax_scale, int32_t cp, int32_t rank, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  const char* where = "cp_attention_bwd";
+  int rc = check_lb(where, seq, cp);
+  if (rc) return rc;
+  if (rank < 0 || rank >= cp) return fail(CPA_EINVAL, "%s: rank %d outside [0, %d)", where, rank, cp);
+  if (batch < 0 || sq < 0) return fail(CPA_EINVAL, "%s: batch and sq must be >= 0", where);
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(CPA_EINVAL, "%s: hq (%d) must be a positive multiple of hkv (%d)", where, hq, hkv);
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(CPA_EINVAL, "%s: softmax_scale must be finite and > 0", where);
+  if (!q_positions && sq != seq / cp)
+    return fail(CPA_EINVAL, "%s: without q_positions, sq (%d) must equal seq/cp (%d)", where, sq, seq / cp);
+  if (dtype != CPA_F32 && dtype != CPA_BF16) return fail(CPA_EINVAL, "%s: unknown dtype %d", where, dtype);
+  if (dtype != CPA_BF16 || !((d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128)))
+    return fail(CPA_ENOTSUP, "%s: (dtype %d, d_qk %d, d_v %d) not supported (bf16 with 64/64 or 128/128)", where,
+                dtype, d_qk, d_v);
+  if ((int64_t)batch * seq * hkv * d_qk * 4 >= (int64_t(1) << 40) ||
+      (int64_t)batch * sq * hq * d_qk * 4 >= (int64_t(1) << 40) || (int64_t)hq * d_qk * 2 * 32 >= (int64_t(1) << 31))
+    return fail(CPA_EINVAL, "%s: tensor too large", where);
+  if (batch == 0 || sq == 0) return CPA_OK;
+  if (!q_shard || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv || !workspace)
+    return fail(CPA_EINVAL, "%s: null pointer", where);
+  if (!aligned16(q_shard) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return fail(CPA_EINVAL, "%s: tensors and workspace must be 16-byte aligned", where);
+  if (((uintptr_t)lse & 3u) || (q_positions && ((uintptr_t)q_positions & 3u)))
+    return fail(CPA_EINVAL, "%s: lse and q_positions must be 4-byte aligned", where);
+  const size_t need = cp_attention_bwd_workspace_bytes(batch, sq, hq);
+  if (workspace_bytes < need)
+    return fail(CPA_EINVAL, "%s: workspace of %zu bytes, need %zu", where, workspace_bytes, need);
+  rc = check_device(where);
+  if (rc) return rc;
+  AttnBwdArgs a;
+  a.q = q_shard;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = d_o;
+  a.q_pos = q_positions;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.ws = workspace;
+  a.batch = batch;
+  a.seq = seq;
+  a.sq = sq;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d_qk = d_qk;
+  a.d_v = d_v;
+  a.cp = cp;
+  a.rank = rank;
+  a.scale = softmax_scale;
+  hipError_t e = launch_attn_bwd_bf16(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, where);
+  return CPA_OK;
+}
+
 size_t gqa_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t max_len, int32_t d) {
   if (batch <= 0 || hq <= 0 || hkv <= 0 || max_len <= 0 || d <= 0) return 0;
   return (size_t)batch * hq * decode_nsplit(max_len) * (size_t)(d + 2) * sizeof(float);

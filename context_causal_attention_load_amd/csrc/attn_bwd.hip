@@ -1,0 +1,670 @@
+// Backward pass of one context-parallel rank's causal grouped-query attention, for gfx950.
+//
+// What it computes ("Add context parallelism", PR 1445, Description: context parallelism is
+// there to train long sequences, so each rank also differentiates its shard's attention over
+// the all-gathered keys and values under the same reordered causal mask). With the forward's
+// O and row log-sum-exp and an upstream gradient dO, by the chain rule:
+//   D_i = dO_i . O_i,  P_ij = exp(s_ij - LSE_i),  dS_ij = P_ij (dO_i . v_j - D_i),
+//   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i,
+// with s_ij = scale q_i . k_j over visible keys and dK, dV of a kv head summed over its query
+// heads. dK and dV cover every gathered key but only this rank's queries (the part a
+// reduce-scatter over ranks would sum).
+//
+// Three launches, bf16 inputs, fp32 accumulation, fp32 gradients:
+//  * prep: D, LSE in log2 units and the rows' positions (padded to 32-row blocks) into the
+//    workspace, plus each 32-row block's smallest and largest position.
+//  * dq: the forward's decomposition (a wave owns one head and 32 query rows; K/V tiles of 64
+//    keys stream through double-buffered LDS by direct-to-LDS copies, visited chunk by chunk
+//    in original order). Per tile: S^T = K Q'^T seeded with -LSE (so the products are the
+//    exponents of P), dP^T - D = V dO^T seeded with -D, dS^T = P^T (dP^T - D) rounded to bf16,
+//    then dQ^T += K^T dS^T with K^T from the transposing LDS read (ds_read_b64_tr_b16).
+//  * dkdv: key-stationary. A workgroup owns 128 keys of one kv head (32 per wave); the keys'
+//    K' (scaled) and V fragments stay in registers as B operands. It streams (32-row query
+//    block, query head) stages of Q, dO, log2-LSE, D and positions through double-buffered LDS,
+//    skipping blocks whose rows are all before the keys. Per stage: S = Q K'^T seeded with
+//    -LSE, dP - D = dO V^T seeded with -D; P and dS come out with a lane per key, already in
+//    the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS, whose A operands are the
+//    transposing LDS reads of the dO and Q tiles.
+#include "attn_tiles.h"
+
+namespace cpattn {
+namespace {
+
+constexpr int kBQ = 32;  // query rows per dkdv stage and per position block
+
+struct BwdExtra {
+  const __bf16* o;
+  const float* lse;
+  const __bf16* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;   // [B, Hq, Sqp]
+  float* lse2;    // [B, Hq, Sqp]
+  int32_t* pos;   // [Sqp]
+  int32_t* blk;   // [2 * nqb]: min positions, then max positions
+  int Sqp, nqb;
+  float scale;
+};
+
+// ---- prep: rows' positions and block bounds (one thread per padded row)
+__global__ __launch_bounds__(256) void bwd_positions_kernel(FwdParams p, BwdExtra e) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= e.Sqp) return;  // Sqp is a multiple of 32: whole 32-lane groups exit together
+  int pos = -1;
+  if (i < p.Sq) {
+    pos = p.qpos ? p.qpos[i] : (int)lb_src((int64_t)p.rank * 2 * p.c + i, p.c, p.cp);
+    pos = pos < 0 ? 0 : (pos > p.S - 1 ? p.S - 1 : pos);
+  }
+  e.pos[i] = pos;
+  int mn = i < p.Sq ? pos : 0x7fffffff, mx = pos;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) {
+    mn = min(mn, __shfl_xor(mn, off, 32));
+    mx = max(mx, __shfl_xor(mx, off, 32));
+  }
+  if ((i & 31) == 0) {
+    e.blk[i / 32] = mn;
+    e.blk[e.nqb + i / 32] = mx;
+  }
+}
+
+// ---- prep: D = dO . O and LSE * log2 e per (b, h, row); 16 lanes per row
+template <int DV>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(FwdParams p, BwdExtra e) {
+  const int64_t r = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;  // (b, h, row) over padded rows
+  const int64_t total = (int64_t)p.B * p.Hq * e.Sqp;
+  if (r >= total) return;
+  const int l16 = threadIdx.x % 16;
+  const int row = (int)(r % e.Sqp);
+  const int64_t bh = r / e.Sqp;
+  const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+  float acc = 0.f;
+  if (row < p.Sq) {
+    const int64_t base = (((int64_t)b * p.Sq + row) * p.Hq + h) * DV;
+    for (int d = l16 * 8; d < DV; d += 128) {
+      const bf16x8 ov = *reinterpret_cast<const bf16x8*>(e.o + base + d);
+      const bf16x8 gv = *reinterpret_cast<const bf16x8*>(e.dout + base + d);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc = __builtin_fmaf((float)ov[t], (float)gv[t], acc);
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (l16 == 0) {
+    e.delta[r] = acc;
+    e.lse2[r] = row < p.Sq ? e.lse[bh * p.Sq + row] * kLog2e : 0.f;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dq kernel
+// ------------------------------------------------------------------------------------------
+template <int DQK, int DV>
+struct DqCfg {
+  static constexpr int BK = 64;
+  static constexpr int KCH = DQK / 8;
+  static constexpr int VCH = DV / 8;
+  static constexpr int K_BYTES = BK * KCH * 16;
+  static constexpr int V_BYTES = BK * VCH * 16;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int K_LOADS = BK * KCH / kThreads;
+  static constexpr int V_LOADS = BK * VCH / kThreads;
+  static_assert(BK * KCH % kThreads == 0 && BK * VCH % kThreads == 0, "tile/thread mismatch");
+  static constexpr int QK_STEPS = DQK / 16;
+  static constexpr int DV_STEPS = DV / 16;
+  static constexpr int MQ = DQK / 32;
+  static constexpr int MB = BK / 32;
+  static constexpr int PKS = BK / 16;
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, BwdExtra e) {
+  using C = DqCfg<DQK, DV>;
+  __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGE];
+  __shared__ int s_red[2 * kWaves];
+
+  WorkItem w;
+  if (!decode_item(p, w)) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int hl = lane / 32;
+  const int head = w.head0 + wave / p.wpr;
+
+  int my_row, my_pos, qmin, qmax;
+  row_positions(p, w, wave, lane, my_row, my_pos, qmin, qmax, s_red);
+  if (qmax < 0) return;
+
+  const float sl2 = p.scale_log2;
+  // Q fragment (scaled, B operand of S^T = K Q'^T) and dO fragment (B operand of V dO^T):
+  // lane holds row (lane & 31), dims 16 ks + 8 hl .. + 7
+  bf16x8 qf[C::QK_STEPS], df[C::DV_STEPS];
+  f32x16 c_lse, c_dlt;
+  {
+    const int row = my_row < p.Sq ? my_row : p.Sq - 1;
+    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.q) +
+                                                         (((int64_t)w.b * p.Sq + row) * p.Hq + head) * DQK);
+    const bf16x8* drow = reinterpret_cast<const bf16x8*>(e.dout + (((int64_t)w.b * p.Sq + row) * p.Hq + head) * DV);
+#pragma unroll
+    for (int ks = 0; ks < C::QK_STEPS; ++ks) {
+      const bf16x8 raw = qrow[2 * ks + hl];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) qf[ks][t] = (__bf16)((float)raw[t] * sl2);
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::DV_STEPS; ++ks) df[ks] = drow[2 * ks + hl];
+    const int64_t sidx = ((int64_t)w.b * p.Hq + head) * e.Sqp + row;
+    const float l2 = e.lse2[sidx], dl = e.delta[sidx];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      c_lse[r] = -l2;
+      c_dlt[r] = -dl;
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::QK_STEPS; ++ks) asm volatile("" ::"v"(qf[ks]));
+#pragma unroll
+    for (int ks = 0; ks < C::DV_STEPS; ++ks) asm volatile("" ::"v"(df[ks]));
+    asm volatile("" ::"v"(c_lse), "v"(c_dlt));
+  }
+
+  const int64_t kv_row_bytes_k = (int64_t)p.Hkv * DQK * 2;
+  const int64_t kv_row_bytes_v = (int64_t)p.Hkv * DV * 2;
+  const char* kbase = static_cast<const char*>(p.k) + (int64_t)w.b * p.S * kv_row_bytes_k + (int64_t)w.g * DQK * 2;
+  const char* vbase = static_cast<const char*>(p.v) + (int64_t)w.b * p.S * kv_row_bytes_v + (int64_t)w.g * DV * 2;
+  const int c = p.c;
+  const int imax = min(qmax / c, 2 * p.cp - 1);
+
+  constexpr int K_DMA = C::K_LOADS, V_DMA = C::V_LOADS;
+  int k_row[K_DMA], v_row[V_DMA];
+  unsigned k_col[K_DMA], v_col[V_DMA];
+#pragma unroll
+  for (int u = 0; u < K_DMA; ++u) {
+    const int pos = (u * kWaves + wave) * 1024 + lane * 16;
+    const int row = pos / (C::KCH * 16), phys = (pos % (C::KCH * 16)) / 16;
+    k_row[u] = row;
+    k_col[u] = (unsigned)((phys ^ swz<C::KCH>(row)) * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < V_DMA; ++u) {
+    const int pos = (u * kWaves + wave) * 1024 + lane * 16;
+    const int row = pos / (C::VCH * 16), phys = (pos % (C::VCH * 16)) / 16;
+    v_row[u] = row;
+    v_col[u] = (unsigned)((phys ^ swz<C::VCH>(row)) * 16);
+  }
+  const unsigned lds0 = (unsigned)(uintptr_t)lds;
+  auto dma_tile = [&](const TileCursor& tc, int b) {
+    const int64_t prow0 = lb_chunk_offset(tc.chunk, c, p.cp) + tc.t0;
+    const int last = min(C::BK, c - tc.t0) - 1;  // rows past a chunk's end re-read its last row
+    const char* kt = kbase + prow0 * kv_row_bytes_k;
+    const char* vt = vbase + prow0 * kv_row_bytes_v;
+    const unsigned kl = lds0 + b * C::STAGE;
+    const unsigned vl = kl + C::K_BYTES;
+#pragma unroll
+    for (int u = 0; u < K_DMA; ++u)
+      dma16_sv(kt, (unsigned)(min(k_row[u], last) * kv_row_bytes_k) + k_col[u], kl + (u * kWaves + wave) * 1024);
+#pragma unroll
+    for (int u = 0; u < V_DMA; ++u)
+      dma16_sv(vt, (unsigned)(min(v_row[u], last) * kv_row_bytes_v) + v_col[u], vl + (u * kWaves + wave) * 1024);
+  };
+
+  f32x16 dqacc[C::MQ];
+#pragma unroll
+  for (int m = 0; m < C::MQ; ++m) dqacc[m] = f32x16{};
+
+  TileCursor tc{0, 0};
+  dma_tile(tc, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int buf = 0;
+  const int grp = lane / 16;
+  const int tr_e = (lane % 16) / 4;
+  const int tr_q = lane % 4;
+
+  while (tc.chunk <= imax) {
+    TileCursor nx = tc;
+    next_tile<C::BK>(nx, c, qmax);
+    const bool has_next = nx.chunk <= imax;
+    if (has_next) dma_tile(nx, buf ^ 1);
+
+    const char* kb = lds + buf * C::STAGE;
+    const char* vb = kb + C::K_BYTES;
+
+    const int kpos0 = tc.chunk * c + tc.t0;
+    const int nvalid = min(C::BK, c - tc.t0);
+    const bool need_mask = (kpos0 + C::BK - 1 > qmin) || (nvalid < C::BK);
+    // key kk of the tile is visible iff kk <= lim (kk < nvalid and kpos0 + kk <= my_pos)
+    const int lim = min(nvalid - 1, my_pos - kpos0) - 4 * hl;
+
+    // one 32-key block at a time: exponents of P (S^T = K Q'^T - LSE), dP^T - D = V dO^T - D,
+    // dS^T rounded to bf16, then its two k-steps of dQ^T += K^T dS^T
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const int krow = mb * 32 + (lane & 31);
+      f32x16 sacc = c_lse;
+      const char* kr = kb + krow * (C::KCH * 16);
+      const int swk = swz<C::KCH>(krow);
+#pragma unroll
+      for (int ks = 0; ks < C::QK_STEPS; ++ks) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + (((2 * ks + hl) ^ swk) * 16));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc, 0, 0, 0);
+      }
+      f32x16 dacc = c_dlt;
+      const char* vr = vb + krow * (C::VCH * 16);
+      const int swv = swz<C::VCH>(krow);
+#pragma unroll
+      for (int ks = 0; ks < C::DV_STEPS; ++ks) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(vr + (((2 * ks + hl) ^ swv) * 16));
+        dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[ks], dacc, 0, 0, 0);
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = mb * 32 + 8 * (r / 4) + (r % 4);
+          sacc[r] = kk <= lim ? sacc[r] : -INFINITY;
+        }
+      }
+      // dS^T in the B-operand layout: k-step j of this block holds registers 8 j .. 8 j + 7
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dsb[r / 8][r % 8] = (__bf16)(__builtin_amdgcn_exp2f(sacc[r]) * dacc[r]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ks = 2 * mb + j;
+        const int row_a = 16 * ks + 4 * (grp / 2) + tr_e;
+        const int row_b = row_a + 8;
+#pragma unroll
+        for (int m = 0; m < C::MQ; ++m) {
+          const int col = 32 * m + 16 * (grp % 2) + 4 * tr_q;
+          const int ch = col / 8, within = (col % 8) * 2;
+          const char* pa = kb + row_a * (C::KCH * 16) + ((ch ^ swz<C::KCH>(row_a)) * 16) + within;
+          const char* pb2 = kb + row_b * (C::KCH * 16) + ((ch ^ swz<C::KCH>(row_b)) * 16) + within;
+          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
+          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
+          typedef short i16x8 __attribute__((ext_vector_type(8)));
+          i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          dqacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), dsb[j], dqacc[m], 0,
+                                                             0, 0);
+        }
+      }
+    }
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    buf ^= 1;
+    tc = nx;
+  }
+
+  if (my_row < p.Sq) {
+    float* og = e.dq + (((int64_t)w.b * p.Sq + my_row) * p.Hq + head) * DQK;
+#pragma unroll
+    for (int m = 0; m < C::MQ; ++m) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        f32x4 ov;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ov[t] = dqacc[m][a4 * 4 + t] * e.scale;
+        *reinterpret_cast<f32x4*>(og + 32 * m + 8 * a4 + 4 * hl) = ov;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dkdv kernel
+// ------------------------------------------------------------------------------------------
+constexpr int kKvWaves = 4;
+constexpr int kKvThreads = kKvWaves * 64;
+constexpr int kBKV = kKvWaves * 32;  // keys per workgroup
+
+template <int DQK, int DV>
+struct DkvCfg {
+  static constexpr int QCH = DQK / 8;
+  static constexpr int OCH = DV / 8;
+  static constexpr int Q_BYTES = kBQ * QCH * 16;
+  static constexpr int O_BYTES = kBQ * OCH * 16;
+  static constexpr int STAT_BYTES = 3 * kBQ * 4;  // log2-LSE, D, positions
+  static constexpr int STAGE = Q_BYTES + O_BYTES + STAT_BYTES;
+  static constexpr int Q_DMA = Q_BYTES / (kKvWaves * 1024);
+  static constexpr int O_DMA = O_BYTES / (kKvWaves * 1024);
+  static_assert(Q_BYTES % (kKvWaves * 1024) == 0 && O_BYTES % (kKvWaves * 1024) == 0, "stage/wave mismatch");
+  static constexpr int QK_STEPS = DQK / 16;
+  static constexpr int DV_STEPS = DV / 16;
+  static constexpr int MK = DQK / 32;
+  static constexpr int MV = DV / 32;
+};
+
+struct DkvParams {
+  int B, S, Sq, Hq, Hkv, G, cp, c, ntc, n_items, per_xcd;
+  float scale_log2;
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(DkvParams p, BwdExtra e) {
+  using C = DkvCfg<DQK, DV>;
+  __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGE];
+
+  // work item: (b, g, chunk i, tile t). Each XCD takes a contiguous range of items, in which
+  // tiles and chunks vary fastest, so an XCD holds whole kv heads (equal work) and its L2 serves
+  // one head group's Q and dO; within the range the earliest positions (keys seen by the most
+  // query rows) are dispatched first.
+  const int bid = blockIdx.x;
+  const int W = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
+  if (W >= p.n_items) return;
+  int t = W;
+  const int tile = t % p.ntc;
+  t /= p.ntc;
+  const int chunk = t % (2 * p.cp);
+  t /= 2 * p.cp;
+  const int g = t % p.Hkv;
+  const int b = t / p.Hkv;
+  const int t0 = tile * kBKV;
+  const int kpos0 = chunk * p.c + t0;
+  const int nvalid = min(kBKV, p.c - t0);
+  const int64_t prow0 = lb_chunk_offset(chunk, p.c, p.cp) + t0;  // gathered slot of key 0
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int hl = lane / 32;
+  const int kk = wave * 32 + (lane & 31);  // this lane's key within the tile
+  const int krow = min(kk, nvalid - 1);
+
+  // K' (scaled) and V fragments, B operands: lane holds key kk, dims 16 ks + 8 hl .. + 7
+  bf16x8 kf[C::QK_STEPS], vf[C::DV_STEPS];
+  {
+    const bf16x8* kr = reinterpret_cast<const bf16x8*>(p.k + (((int64_t)b * p.S + prow0 + krow) * p.Hkv + g) * DQK);
+    const bf16x8* vr = reinterpret_cast<const bf16x8*>(p.v + (((int64_t)b * p.S + prow0 + krow) * p.Hkv + g) * DV);
+#pragma unroll
+    for (int ks = 0; ks < C::QK_STEPS; ++ks) {
+      const bf16x8 raw = kr[2 * ks + hl];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kf[ks][u] = (__bf16)((float)raw[u] * p.scale_log2);
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::DV_STEPS; ++ks) vf[ks] = vr[2 * ks + hl];
+#pragma unroll
+    for (int ks = 0; ks < C::QK_STEPS; ++ks) asm volatile("" ::"v"(kf[ks]));
+#pragma unroll
+    for (int ks = 0; ks < C::DV_STEPS; ++ks) asm volatile("" ::"v"(vf[ks]));
+  }
+
+  f32x16 dkacc[C::MK], dvacc[C::MV];
+#pragma unroll
+  for (int m = 0; m < C::MK; ++m) dkacc[m] = f32x16{};
+#pragma unroll
+  for (int m = 0; m < C::MV; ++m) dvacc[m] = f32x16{};
+
+  // stages: (query block qb, head h of the group); blocks whose rows all precede the keys skip
+  const int* blkmin = e.blk;
+  const int* blkmax = e.blk + e.nqb;
+  auto next_visible = [&](int qb) {
+    while (qb < e.nqb && blkmax[qb] < kpos0) ++qb;
+    return qb;
+  };
+
+  const int64_t q_row_bytes = (int64_t)p.Hq * DQK * 2;
+  const int64_t o_row_bytes = (int64_t)p.Hq * DV * 2;
+  const char* qbase = reinterpret_cast<const char*>(p.q) + (int64_t)b * p.Sq * q_row_bytes;
+  const char* obase = reinterpret_cast<const char*>(e.dout) + (int64_t)b * p.Sq * o_row_bytes;
+  const unsigned lds0 = (unsigned)(uintptr_t)lds;
+  // per-lane DMA geometry: wave-instruction u of a stage fills LDS bytes
+  // [1024 (u * kKvWaves + wave), + 1024) of the Q (or dO) tile; lane l at + 16 l
+  auto dma_stage = [&](int qb, int h, int bufi) {
+    const unsigned ql = lds0 + bufi * C::STAGE;
+    const unsigned ol = ql + C::Q_BYTES;
+    const unsigned sl = ol + C::O_BYTES;
+    const int last = p.Sq - 1 - qb * kBQ;  // rows past the shard re-read its last row
+    const char* qt = qbase + (int64_t)qb * kBQ * q_row_bytes + (int64_t)h * DQK * 2;
+    const char* ot = obase + (int64_t)qb * kBQ * o_row_bytes + (int64_t)h * DV * 2;
+#pragma unroll
+    for (int u = 0; u < C::Q_DMA; ++u) {
+      const int pos = (u * kKvWaves + wave) * 1024 + lane * 16;
+      const int row = pos / (C::QCH * 16), phys = (pos % (C::QCH * 16)) / 16;
+      const unsigned off = (unsigned)(min(row, last) * q_row_bytes) + (unsigned)((phys ^ swz<C::QCH>(row)) * 16);
+      dma16_sv(qt, off, ql + (u * kKvWaves + wave) * 1024);
+    }
+#pragma unroll
+    for (int u = 0; u < C::O_DMA; ++u) {
+      const int pos = (u * kKvWaves + wave) * 1024 + lane * 16;
+      const int row = pos / (C::OCH * 16), phys = (pos % (C::OCH * 16)) / 16;
+      const unsigned off = (unsigned)(min(row, last) * o_row_bytes) + (unsigned)((phys ^ swz<C::OCH>(row)) * 16);
+      dma16_sv(ot, off, ol + (u * kKvWaves + wave) * 1024);
+    }
+    // log2-LSE, D and positions of the block's 32 rows: 3 x 128 bytes, 8 lanes each
+    if (wave == 0 && lane < 24) {
+      const int which = lane / 8, part = lane % 8;
+      const int64_t sidx = ((int64_t)b * p.Hq + h) * e.Sqp + qb * kBQ;
+      const char* src = which == 0 ? reinterpret_cast<const char*>(e.lse2 + sidx)
+                                   : (which == 1 ? reinterpret_cast<const char*>(e.delta + sidx)
+                                                 : reinterpret_cast<const char*>(e.pos + qb * kBQ));
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src + part * 16),
+                   "s"(__builtin_amdgcn_readfirstlane(sl)) : "memory", "m0");
+    }
+  };
+
+  const int grp = lane / 16;
+  const int tr_e = (lane % 16) / 4;
+  const int tr_q = lane % 4;
+  const int kpos = kpos0 + kk;
+
+  int qb = next_visible(0), h = 0;
+  if (qb < e.nqb) {
+    dma_stage(qb, g * p.G, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  int buf = 0;
+  while (qb < e.nqb) {
+    int nqb = qb, nh = h + 1;
+    if (nh == p.G) {
+      nh = 0;
+      nqb = next_visible(qb + 1);
+    }
+    if (nqb < e.nqb) dma_stage(nqb, g * p.G + nh, buf ^ 1);
+
+    const char* qt = lds + buf * C::STAGE;
+    const char* ot = qt + C::Q_BYTES;
+    const float* st_lse = reinterpret_cast<const float*>(ot + C::O_BYTES);
+    const float* st_dlt = st_lse + kBQ;
+    const int* st_pos = reinterpret_cast<const int*>(st_dlt + kBQ);
+
+    // seeds: -log2 LSE and -D of the rows this lane's outputs hold (rows 8 i + 4 hl + j)
+    f32x16 sacc, dacc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(st_lse + 8 * i + 4 * hl);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st_dlt + 8 * i + 4 * hl);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sacc[4 * i + j] = -l4[j];
+        dacc[4 * i + j] = -d4[j];
+      }
+    }
+    // S = Q K'^T - LSE and dP - D = dO V^T - D: A operands are rows of the Q / dO tiles
+    {
+      const int row = lane & 31;
+      const char* qr = qt + row * (C::QCH * 16);
+      const int swq = swz<C::QCH>(row);
+#pragma unroll
+      for (int ks = 0; ks < C::QK_STEPS; ++ks) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + (((2 * ks + hl) ^ swq) * 16));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
+      }
+      const char* orow = ot + row * (C::OCH * 16);
+      const int swo = swz<C::OCH>(row);
+#pragma unroll
+      for (int ks = 0; ks < C::DV_STEPS; ++ks) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + (((2 * ks + hl) ^ swo) * 16));
+        dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dacc, 0, 0, 0);
+      }
+    }
+    // mask where a row does not see the key (or the key is past the tile's valid keys)
+    const bool need_mask = blkmin[qb] < kpos0 + kBKV - 1 || nvalid < kBKV || (qb + 1) * kBQ > p.Sq;
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int4 q4 = *reinterpret_cast<const int4*>(st_pos + 8 * i + 4 * hl);
+        const int qp[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sacc[4 * i + j] = (kk < nvalid && kpos <= qp[j]) ? sacc[4 * i + j] : -INFINITY;
+      }
+    }
+    // P and dS, bf16, in the B-operand layout of the two products below (k-step ks: rows
+    // 16 ks + 8 (t / 4) + 4 hl + t % 4 in register t)
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = __builtin_amdgcn_exp2f(sacc[r]);
+      pb[r / 8][r % 8] = (__bf16)pr;
+      dsb[r / 8][r % 8] = (__bf16)(pr * dacc[r]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, A operands from transposing reads of the tiles
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int row_a = 16 * ks + 4 * (grp / 2) + tr_e;
+      const int row_b = row_a + 8;
+#pragma unroll
+      for (int m = 0; m < C::MV; ++m) {
+        const int col = 32 * m + 16 * (grp % 2) + 4 * tr_q;
+        const int ch = col / 8, within = (col % 8) * 2;
+        const char* pa = ot + row_a * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_a)) * 16) + within;
+        const char* pb2 = ot + row_b * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_b)) * 16) + within;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[ks], dvacc[m], 0, 0,
+                                                           0);
+      }
+#pragma unroll
+      for (int m = 0; m < C::MK; ++m) {
+        const int col = 32 * m + 16 * (grp % 2) + 4 * tr_q;
+        const int ch = col / 8, within = (col % 8) * 2;
+        const char* pa = qt + row_a * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_a)) * 16) + within;
+        const char* pb2 = qt + row_b * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_b)) * 16) + within;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), dsb[ks], dkacc[m], 0, 0,
+                                                           0);
+      }
+    }
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    buf ^= 1;
+    qb = nqb;
+    h = nh;
+  }
+
+  // dK = scale dK^T, dV; lane holds key kk, dims 32 m + 8 a4 + 4 hl + t
+  if (kk < nvalid) {
+    float* dkr = e.dk + (((int64_t)b * p.S + prow0 + kk) * p.Hkv + g) * DQK;
+    float* dvr = e.dv + (((int64_t)b * p.S + prow0 + kk) * p.Hkv + g) * DV;
+#pragma unroll
+    for (int m = 0; m < C::MK; ++m) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        f32x4 ov;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ov[u] = dkacc[m][a4 * 4 + u] * e.scale;
+        *reinterpret_cast<f32x4*>(dkr + 32 * m + 8 * a4 + 4 * hl) = ov;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < C::MV; ++m) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        f32x4 ov;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ov[u] = dvacc[m][a4 * 4 + u];
+        *reinterpret_cast<f32x4*>(dvr + 32 * m + 8 * a4 + 4 * hl) = ov;
+      }
+    }
+  }
+}
+
+template <int DQK, int DV>
+hipError_t launch_bwd_typed(const AttnBwdArgs& a, hipStream_t stream) {
+  AttnArgs fa;
+  fa.q = a.q;
+  fa.k = a.k;
+  fa.v = a.v;
+  fa.q_pos = a.q_pos;
+  fa.o = nullptr;
+  fa.lse = nullptr;
+  fa.batch = a.batch;
+  fa.seq = a.seq;
+  fa.sq = a.sq;
+  fa.hq = a.hq;
+  fa.hkv = a.hkv;
+  fa.d_qk = DQK;
+  fa.d_v = DV;
+  fa.cp = a.cp;
+  fa.rank = a.rank;
+  fa.scale = a.scale;
+  const FwdParams p = make_params(fa);
+
+  BwdExtra e;
+  e.o = static_cast<const __bf16*>(a.o);
+  e.lse = a.lse;
+  e.dout = static_cast<const __bf16*>(a.dout);
+  e.dq = a.dq;
+  e.dk = a.dk;
+  e.dv = a.dv;
+  const int Sqp = (a.sq + kBQ - 1) / kBQ * kBQ;
+  e.Sqp = Sqp;
+  e.nqb = Sqp / kBQ;
+  e.scale = a.scale;
+  char* ws = static_cast<char*>(a.ws);
+  const size_t stat_bytes = (size_t)a.batch * a.hq * Sqp * 4;
+  e.delta = reinterpret_cast<float*>(ws);
+  e.lse2 = reinterpret_cast<float*>(ws + stat_bytes);
+  e.pos = reinterpret_cast<int32_t*>(ws + 2 * stat_bytes);
+  e.blk = reinterpret_cast<int32_t*>(ws + 2 * stat_bytes + (size_t)Sqp * 4);
+
+  hipLaunchKernelGGL(bwd_positions_kernel, dim3((Sqp + 255) / 256), dim3(256), 0, stream, p, e);
+  const int64_t rows = (int64_t)a.batch * a.hq * Sqp;
+  hipLaunchKernelGGL((bwd_delta_kernel<DV>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p, e);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV>), dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, stream, p, e);
+
+  DkvParams d;
+  d.B = a.batch;
+  d.S = a.seq;
+  d.Sq = a.sq;
+  d.Hq = a.hq;
+  d.Hkv = a.hkv;
+  d.G = a.hq / a.hkv;
+  d.cp = a.cp;
+  d.c = a.seq / (2 * a.cp);
+  d.ntc = (d.c + kBKV - 1) / kBKV;
+  d.n_items = 2 * a.cp * d.B * d.Hkv * d.ntc;
+  d.per_xcd = (d.n_items + kNumXcd - 1) / kNumXcd;
+  d.scale_log2 = a.scale * kLog2e;
+  d.q = static_cast<const __bf16*>(a.q);
+  d.k = static_cast<const __bf16*>(a.k);
+  d.v = static_cast<const __bf16*>(a.v);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV>), dim3(d.per_xcd * kNumXcd), dim3(kKvThreads), 0, stream, d, e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(int batch, int sq, int hq) {
+  const size_t sqp = ((size_t)sq + kBQ - 1) / kBQ * kBQ;
+  return 2 * (size_t)batch * hq * sqp * 4 + sqp * 4 + 2 * (sqp / kBQ) * 4;
+}
+
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
+  if (a.batch == 0 || a.sq == 0) return hipSuccess;
+  if (a.d_qk == 128 && a.d_v == 128) return launch_bwd_typed<128, 128>(a, stream);
+  if (a.d_qk == 64 && a.d_v == 64) return launch_bwd_typed<64, 64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cpattn

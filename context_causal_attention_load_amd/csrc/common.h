@@ -70,6 +70,24 @@ struct AttnArgs {
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream);
 
+struct AttnBwdArgs {
+  const void* q;          // [B, Sq, Hq, Dqk] bf16
+  const void* k;          // [B, S, Hkv, Dqk] bf16, gathered order
+  const void* v;          // [B, S, Hkv, Dv] bf16
+  const void* o;          // [B, Sq, Hq, Dv] bf16, forward output
+  const float* lse;       // [B, Hq, Sq], forward row log-sum-exp (natural log)
+  const void* dout;       // [B, Sq, Hq, Dv] bf16
+  const int32_t* q_pos;   // may be null: positions from (cp, rank)
+  float* dq;              // [B, Sq, Hq, Dqk]
+  float* dk;              // [B, S, Hkv, Dqk]
+  float* dv;              // [B, S, Hkv, Dv]
+  void* ws;               // attn_bwd_workspace_bytes(batch, sq, hq) bytes
+  int batch, seq, sq, hq, hkv, d_qk, d_v, cp, rank;
+  float scale;
+};
+size_t attn_bwd_workspace_bytes(int batch, int sq, int hq);
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream);
+
 struct DecodeArgs {
   const void* q;
   const void* k;

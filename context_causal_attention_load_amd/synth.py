@@ -16,7 +16,8 @@ shapes are used; values are N(0, 1).
 Recipe: ``torch.Generator("cpu").manual_seed(seed)``; Q, then K, then V are drawn as
 float32 N(0,1) in natural token order, token chunk by token chunk (``TOKEN_CHUNK`` tokens
 per draw, all batches of a chunk at once), then rounded to the workload dtype with
-round-to-nearest-even (``Tensor.to``). Decode draws ``lengths`` (uniform integers in
+round-to-nearest-even (``Tensor.to``). The backward pass's upstream gradient dO is drawn the same way as Q from a generator of its own
+(seed + 1000 for a named workload). Decode draws ``lengths`` (uniform integers in
 [len_min, len_max]) first, then q, then the K cache and the V cache over the full maximum
 length. The int8-cache decode draws ``lengths`` and q the same way, then for K and then V
 the codes (float32 N(0,1) times 40, rounded, clipped to [-127, 127]: the spread of absmax-int8
@@ -97,6 +98,17 @@ def prefill_inputs(batch, seq, hq, hkv, d_qk, d_v, dtype, seed):
     k = _draw(gen, (batch, seq, hkv, d_qk), dtype)
     v = _draw(gen, (batch, seq, hkv, d_v), dtype)
     return q, k, v
+
+
+def prefill_grad(batch, seq, hq, d_v, dtype, seed):
+    """Upstream gradient dO [B, S, Hq, Dv] for the backward pass, N(0,1) in natural token order,
+    drawn like Q from its own generator (seeded with ``seed``)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    return _draw(gen, (batch, seq, hq, d_v), dtype)
+
+
+def workload_prefill_grad(w: PrefillWorkload, seed=None):
+    return prefill_grad(w.batch, w.seq, w.hq, w.d_v, w.dtype, 1000 + (w.seed if seed is None else seed))
 
 
 def workload_prefill_inputs(w: PrefillWorkload, seed=None):

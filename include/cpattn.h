@@ -128,6 +128,38 @@ int cp_attention_fwd(const void* q_shard, const void* k, const void* v,
                      int32_t cp, int32_t rank, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Backward pass of cp_attention_fwd for one rank ("Add context parallelism", PR 1445,
+ * Description: context parallelism serves training on long sequences, so each rank also
+ * differentiates its shard's attention). From the forward's inputs, its O and LSE, and the
+ * upstream gradient dO (the chain rule through the forward's definition):
+ *   D_i = dO_i . O_i,  P_ij = exp(scale q_i . k_j - LSE_i) over visible keys,
+ *   dS_ij = P_ij (dO_i . v_j - D_i),  dQ_i = scale sum_j dS_ij k_j,
+ *   dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i,
+ * with dK and dV of a kv head summed over the query heads of its group. dK and dV cover every
+ * key of the gathered K/V but only this rank's query rows: summing them over the ranks (a
+ * reduce-scatter on several GPUs) gives the full gradients.
+ *
+ *   q_shard, k, v, q_positions, batch, seq, sq, hq, hkv, d_qk, d_v, softmax_scale, cp, rank:
+ *            exactly as passed to cp_attention_fwd
+ *   o        [B, Sq, Hq, Dv] and lse [B, Hq, Sq] float32: that forward call's outputs
+ *   d_o      [B, Sq, Hq, Dv], dtype of q
+ *   dq       [B, Sq, Hq, Dqk] float32 (output)
+ *   dk, dv   [B, seq, Hkv, Dqk | Dv] float32 (output), in the gathered key order
+ *   workspace, workspace_bytes: at least cp_attention_bwd_workspace_bytes(batch, sq, hq) bytes of
+ *            caller-owned device scratch; contents on entry do not matter; calls sharing one
+ *            workspace must not overlap.
+ * Supported: bf16 with (d_qk, d_v) in {(64, 64), (128, 128)}; CPA_ENOTSUP otherwise. CPA_EINVAL
+ * for the forward's argument errors, null pointers (all tensors are required), tensors not
+ * 16-byte aligned (lse and q_positions: 4-byte), or a workspace that is too small. */
+size_t cp_attention_bwd_workspace_bytes(int32_t batch, int32_t sq, int32_t hq);
+
+int cp_attention_bwd(const void* q_shard, const void* k, const void* v, const void* o, const float* lse,
+                     const void* d_o, const int32_t* q_positions, float* dq, float* dk, float* dv,
+                     int32_t batch, int32_t seq, int32_t sq, int32_t hq, int32_t hkv, int32_t d_qk,
+                     int32_t d_v, int32_t dtype, float softmax_scale, int32_t cp, int32_t rank,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Grouped-query single-token decode attention ("Add Pallas GPU decode attention in Maxtext
  * inference", PR 1066, Description: decode calls a grouped-query attention kernel; Tests: the
  * cache is filled by a prefill and grows to the target length). The newest token attends to

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
     for must in ("cp_load_balance_permute", "cp_load_balance_unpermute", "cp_attention_fwd",
                  "gqa_decode_attention", "gqa_decode_workspace_bytes", "cpattn_last_error",
                  "cp_load_balance_source_index", "cp_load_balance_positions", "gqa_decode_merge",
-                 "gqa_decode_attention_int8kv", "kv_cache_quantize_int8"):
+                 "gqa_decode_attention_int8kv", "kv_cache_quantize_int8", "cp_attention_bwd",
+                 "cp_attention_bwd_workspace_bytes"):
         assert must in names, names
 
 
@@ -128,6 +129,48 @@ def test_attention_argument_errors(lib, kw, status, substr):
 def test_attention_empty_is_ok_without_device(lib):
     assert _fwd(lib, batch=0)[0] == 0
     assert _fwd(lib, sq=0, pos=FAKE)[0] == 0
+
+
+def _bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, pos=None, dq=FAKE, dk=FAKE, dv=FAKE, batch=1,
+             seq=512, sq=256, hq=4, hkv=2, dqk=64, dv_=64, dtype=binding.CPA_BF16, scale=0.125, cp=2, rank=0,
+             ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    rc = lib.cp_attention_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["pos"], a["dq"], a["dk"],
+                              a["dv"], a["batch"], a["seq"], a["sq"], a["hq"], a["hkv"], a["dqk"], a["dv_"],
+                              a["dtype"], a["scale"], a["cp"], a["rank"], a["ws"], a["ws_bytes"], None)
+    return _status_and_message(lib, rc)
+
+
+@pytest.mark.parametrize("kw,status,substr", [
+    (dict(seq=502), binding.CPA_EINVAL, "multiple of 2*cp"),
+    (dict(rank=2), binding.CPA_EINVAL, "rank"),
+    (dict(hq=3), binding.CPA_EINVAL, "multiple of hkv"),
+    (dict(scale=-0.5), binding.CPA_EINVAL, "softmax_scale"),
+    (dict(sq=100), binding.CPA_EINVAL, "without q_positions"),
+    (dict(dtype=binding.CPA_F32), binding.CPA_ENOTSUP, "not supported"),
+    (dict(dqk=192, dv_=128), binding.CPA_ENOTSUP, "not supported"),
+    (dict(dtype=5), binding.CPA_EINVAL, "dtype"),
+    (dict(lse=None), binding.CPA_EINVAL, "null"),
+    (dict(dk=ctypes.c_void_p(4100)), binding.CPA_EINVAL, "aligned"),
+    (dict(lse=ctypes.c_void_p(4098)), binding.CPA_EINVAL, "aligned"),
+    (dict(ws_bytes=64), binding.CPA_EINVAL, "workspace"),
+])
+def test_attention_bwd_argument_errors(lib, kw, status, substr):
+    rc, msg = _bwd(lib, **kw)
+    assert rc == status and substr in msg, (rc, msg)
+
+
+def test_attention_bwd_empty_is_ok_without_device(lib):
+    assert _bwd(lib, batch=0)[0] == 0
+    assert _bwd(lib, sq=0, pos=FAKE)[0] == 0
+
+
+def test_attention_bwd_workspace_size(lib):
+    # log2-LSE and D per (b, h, padded row), positions per padded row, min/max per 32-row block
+    assert cpa.attention_bwd_workspace_bytes(1, 16384, 64) == 2 * 64 * 16384 * 4 + 16384 * 4 + 2 * 512 * 4
+    assert cpa.attention_bwd_workspace_bytes(2, 100, 4) == 2 * 2 * 4 * 128 * 4 + 128 * 4 + 2 * 4 * 4
+    assert cpa.attention_bwd_workspace_bytes(0, 100, 4) == 0
 
 
 def _dec(lib, **kw):

@@ -517,3 +517,115 @@ def test_quantize_then_decode_int8():
     O_ref, L_ref = oq.decode_int8_ref(q, kq_r, ks_r, vq_r, vs_r, lengths.numpy(), 1.0 / math.sqrt(128))
     assert_close(o.float().cpu().numpy(), O_ref, 2e-2, "quantize + int8 decode O")
     assert_close(lse.cpu().numpy(), L_ref, 2e-2, "quantize + int8 decode LSE")
+
+
+# ----------------------------------------------------------------------------- backward
+
+from oracle import backward as obw  # noqa: E402
+
+
+def bwd_tol(ref):
+    """bf16 gradients: |err| <= 2e-2 * max(1, max |ref|) (bf16 P, dS and inputs; fp32 sums)."""
+    return 2e-2 * max(1.0, float(np.abs(ref).max()))
+
+
+def run_bwd_rank(qd, kd, vd, dod, seq, cp, rank, scale, kp=None, vp=None):
+    """GPU: permute the shard's Q and dO and the full K/V, forward, then backward."""
+    c = seq // (2 * cp)
+    if kp is None:
+        kp, vp = cpa.permute(kd, cp), cpa.permute(vd, cp)
+    qs = cpa.permute(qd, cp, row_begin=rank * 2 * c, row_count=2 * c)
+    dos = cpa.permute(dod, cp, row_begin=rank * 2 * c, row_count=2 * c)
+    o, lse = cpa.attention_fwd(qs, kp, vp, cp, rank, scale=scale)
+    dq, dk, dv = cpa.attention_bwd(qs, kp, vp, o, lse, dos, cp, rank, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check_bwd_full(batch, seq, cp, hq, hkv, d, ranks, seed, tag):
+    q, k, v = synth.prefill_inputs(batch, seq, hq, hkv, d, d, torch.bfloat16, seed)
+    do = synth.prefill_grad(batch, seq, hq, d, torch.bfloat16, seed + 1000)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    kp, vp = cpa.permute(kd, cp), cpa.permute(vd, cp)
+    perm = olb.load_balance_perm(seq, cp)
+    scale = 1.0 / math.sqrt(d)
+    c = seq // (2 * cp)
+    for r in ranks:
+        announce(f"backward {tag} cp={cp} rank={r}")
+        dq, dk, dv = run_bwd_rank(qd, kd, vd, dod, seq, cp, r, scale, kp, vp)
+        rows = perm[r * 2 * c:(r + 1) * 2 * c]
+        dq_r, dk_r, dv_r = obw.causal_attention_bwd_ref(q[:, rows], k[:, perm], v[:, perm], do[:, rows], rows, perm,
+                                                        scale)
+        assert_close(dq.cpu().numpy(), dq_r, bwd_tol(dq_r), f"dQ {tag} r{r}")
+        assert_close(dk.cpu().numpy(), dk_r, bwd_tol(dk_r), f"dK {tag} r{r}")
+        assert_close(dv.cpu().numpy(), dv_r, bwd_tol(dv_r), f"dV {tag} r{r}")
+
+
+@pytest.mark.parametrize("batch,seq,cp,hq,hkv,d,ranks", [
+    (1, 512, 2, 4, 2, 64, (0, 1)),
+    (2, 400, 2, 4, 1, 128, (0, 1)),     # c = 100: partial key tiles and query blocks
+    (1, 1024, 4, 16, 2, 128, (0, 3)),   # G = 8
+    (1, 256, 1, 2, 2, 64, (0,)),        # cp = 1: plain causal attention
+])
+def test_backward_small(batch, seq, cp, hq, hkv, d, ranks):
+    check_bwd_full(batch, seq, cp, hq, hkv, d, ranks, seed=seq + hq, tag=f"B{batch} S{seq} Hq{hq}/{hkv} D{d}")
+
+
+def test_backward_contiguous_shard_positions():
+    """Explicit q_positions: a contiguous (unbalanced) shard of the natural order, K/V natural."""
+    seq, hq, hkv, d = 512, 4, 2, 64
+    q, k, v = synth.prefill_inputs(1, seq, hq, hkv, d, d, torch.bfloat16, 17)
+    do = synth.prefill_grad(1, seq, hq, d, torch.bfloat16, 18)
+    rows = np.arange(256, 512)
+    pos = torch.tensor(rows, dtype=torch.int32, device=DEV)
+    announce("backward contiguous shard with explicit positions")
+    qs, dos = q[:, 256:].contiguous().to(DEV), do[:, 256:].contiguous().to(DEV)
+    kd, vd = k.to(DEV), v.to(DEV)
+    o, lse = cpa.attention_fwd(qs, kd, vd, 1, 0, q_positions=pos, scale=0.125)
+    dq, dk, dv = cpa.attention_bwd(qs, kd, vd, o, lse, dos, 1, 0, q_positions=pos, scale=0.125)
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = obw.causal_attention_bwd_ref(q[:, 256:], k, v, do[:, 256:], rows, np.arange(seq), 0.125)
+    assert_close(dq.cpu().numpy(), dq_r, bwd_tol(dq_r), "dQ contiguous")
+    assert_close(dk.cpu().numpy(), dk_r, bwd_tol(dk_r), "dK contiguous")
+    assert_close(dv.cpu().numpy(), dv_r, bwd_tol(dv_r), "dV contiguous")
+
+
+def test_backward_llama7b_s8192():
+    w = synth.LLAMA2_7B_S8K
+    check_bwd_full(w.batch, w.seq, 4, w.hq, w.hkv, w.d_qk, (0, 3), seed=w.seed, tag=w.name)
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_backward_llama70b_full_size_sampled(rank):
+    """131072 tokens, cp = 8, one rank at its real shape. dQ on sampled rows; dK, dV at the keys
+    of the last 48 positions of the rank's upper chunk (seen only by the rank's rows at those
+    positions, all of which are in the sample); keys past the rank's last position are exactly
+    0; and dK sums to ~0 over the keys of each kv head (the softmax gradient sums to zero)."""
+    w = synth.LLAMA31_70B_S131K
+    cp, S = 8, w.seq
+    c = S // (2 * cp)
+    announce(f"backward {w.name} rank {rank} (sampled)")
+    q, k, v = synth.workload_prefill_inputs(w)
+    do = synth.workload_prefill_grad(w)
+    perm = olb.load_balance_perm(S, cp)
+    scale = w.scale
+    dq, dk, dv = run_bwd_rank(q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), S, cp, rank, scale)
+    shard = perm[rank * 2 * c:(rank + 1) * 2 * c]
+    top = (2 * cp - rank) * c            # one past the rank's last position
+    p0 = top - 48
+    rng = np.random.default_rng(rank)
+    sel = np.unique(np.concatenate([np.arange(2 * c - 48, 2 * c), rng.integers(0, 2 * c, 8)]))
+    rows = shard[sel]
+    dq_r, dk_r, dv_r = obw.causal_attention_bwd_ref(q[:, rows], k[:, perm], v[:, perm], do[:, rows], rows, perm, scale)
+    assert_close(dq[:, sel].cpu().numpy(), dq_r, bwd_tol(dq_r), f"dQ rank {rank} sampled rows")
+    inv = olb.inverse_perm(perm)
+    keys = inv[p0:top]
+    assert_close(dk[:, keys].cpu().numpy(), dk_r[:, keys], bwd_tol(dk_r[:, keys]), f"dK rank {rank} last keys")
+    assert_close(dv[:, keys].cpu().numpy(), dv_r[:, keys], bwd_tol(dv_r[:, keys]), f"dV rank {rank} last keys")
+    if top < S:
+        later = inv[top:S:997]
+        assert float(dk[:, later].abs().max()) == 0.0 and float(dv[:, later].abs().max()) == 0.0
+    ssum = dk.sum(dim=1).abs().max().item()
+    scale_ref = dk.abs().sum(dim=1).max().item()
+    print(f"  sum_j dK_j: max |.| {ssum:.3e} against max sum_j |dK_j| {scale_ref:.3e}", flush=True)
+    assert ssum <= 1e-2 * scale_ref

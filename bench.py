@@ -12,7 +12,8 @@ Step i runs rank i % cp, so the timed steps cover every rank; per-rank times are
 
 After the timed steps (not part of them): every rank's attention kernel with the balanced
 shard and with a contiguous shard of the natural order, to show the spread the load balance
-removes (`load_balance`; skip with --no-balance-demo).
+removes (`load_balance`; skip with --no-balance-demo); and every rank's backward call
+(`backward`; skip with --no-backward).
 
 Also measured: GQA decode (Mixtral-8x22B shape, batch 24, 48/8 heads, D 128, cache 2048 with
 lengths uniform in [1024, 2048]), rotating 4 cache copies so reads come from HBM rather than
@@ -71,7 +72,7 @@ def useful_flops(seq, cp, hq, dqk, dv, batch=1):
     return 2.0 * pairs * hq * (dqk + dv) * batch
 
 
-def bench_prefill(w, cp, steps, warmup, dev, balance_demo=True):
+def bench_prefill(w, cp, steps, warmup, dev, balance_demo=True, backward=True):
     import context_causal_attention_load_amd as cpa
     from context_causal_attention_load_amd import synth
 
@@ -123,7 +124,50 @@ def bench_prefill(w, cp, steps, warmup, dev, balance_demo=True):
                flops=useful_flops(S, cp, w.hq, w.d_qk, w.d_v, w.batch))
     if balance_demo:
         out["balance"] = balance_demo_ms(w, cp, qd, kd, vd, kp, vp, q_shard, o_shard, lse_shard)
+    if backward:
+        out["backward"] = backward_ms(w, cp, kp, vp, qd, q_shard, o_shard, lse_shard)
     return out
+
+
+def backward_flops(seq, cp, hq, dqk, dv, batch=1):
+    """Useful backward flops of one rank: the five products over visible (query, key, head)
+    triples, S = QK^T and dQ, dK (2 Dqk each), dP = dO V^T and dV (2 Dv each)."""
+    c = seq // (2 * cp)
+    return 2.0 * c * (seq + 1) * hq * (3 * dqk + 2 * dv) * batch
+
+
+def backward_ms(w, cp, kp, vp, qd, q_shard, o_shard, lse_shard):
+    """After the timed forward steps: for every rank, its forward (untimed) then its backward call
+    (prep + dq + dkdv kernels), timed with HIP events on the launch stream. dO is a seeded
+    N(0,1) draw on the device (timing only)."""
+    import context_causal_attention_load_amd as cpa
+
+    S, c = w.seq, w.seq // (2 * cp)
+    gen = torch.Generator(device=qd.device).manual_seed(1000 + w.seed)
+    d_o = torch.randn((w.batch, 2 * c, w.hq, w.d_v), generator=gen, device=qd.device, dtype=torch.float32).to(w.dtype)
+    dq = torch.empty((w.batch, 2 * c, w.hq, w.d_qk), dtype=torch.float32, device=qd.device)
+    dk = torch.empty((w.batch, S, w.hkv, w.d_qk), dtype=torch.float32, device=qd.device)
+    dv = torch.empty((w.batch, S, w.hkv, w.d_v), dtype=torch.float32, device=qd.device)
+    ws = torch.empty(cpa.attention_bwd_workspace_bytes(w.batch, 2 * c, w.hq), dtype=torch.uint8, device=qd.device)
+
+    def run(r, ev=None):
+        cpa.permute(qd, cp, row_begin=r * 2 * c, row_count=2 * c, out=q_shard)
+        cpa.attention_fwd(q_shard, kp, vp, cp, r, scale=w.scale, out=o_shard, lse=lse_shard)
+        if ev is not None:
+            ev[0].record()
+        cpa.attention_bwd(q_shard, kp, vp, o_shard, lse_shard, d_o, cp, r, scale=w.scale, workspace=ws, dq=dq,
+                          dk=dk, dv=dv)
+        if ev is not None:
+            ev[1].record()
+
+    run(0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cp)]
+    for r in range(cp):
+        run(r, evs[r])
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return dict(ms=ms, flops=backward_flops(S, cp, w.hq, w.d_qk, w.d_v, w.batch))
 
 
 def balance_demo_ms(w, cp, qd, kd, vd, kp, vp, q_shard, o_shard, lse_shard):
@@ -266,6 +310,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass timing (after the timed forward steps)")
     ap.add_argument("--no-balance-demo", action="store_true",
                     help="skip the per-rank balanced vs contiguous shard timing (after the timed steps)")
     args = ap.parse_args()
@@ -282,7 +328,8 @@ def main():
     dev = "cuda:0"
     w = synth.LLAMA31_70B_S131K
     cp = w.cps[0]
-    pre = bench_prefill(w, cp, args.steps, args.warmup, dev, balance_demo=not args.no_balance_demo)
+    pre = bench_prefill(w, cp, args.steps, args.warmup, dev, balance_demo=not args.no_balance_demo,
+                        backward=not args.no_backward)
     ms_per_step = sum(pre["step_ms"]) / len(pre["step_ms"])
     value = pre["flops"] / (ms_per_step * 1e-3) / 1e12
     attn_avg_ms = sum(pre["attn_ms"]) / len(pre["attn_ms"])
@@ -307,7 +354,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic("attn_fwd_bf16_llama70b_s131072_cp8.md",
-                                                 ("attn_fwd.hip", "common.h")),
+                                                 ("attn_fwd.hip", "attn_tiles.h", "common.h")),
                      "traffic_unit": "HBM bytes per launch",
                      "kernel": "attn_fwd_bf16_kernel<128,128>", "kernel_avg_ms": round(attn_avg_ms, 4),
                      "useful_flop_per_launch": pre["flops"]},
@@ -315,6 +362,21 @@ def main():
     }
     if "balance" in pre:
         result["load_balance"] = pre["balance"]
+    if "backward" in pre:
+        bw = pre["backward"]
+        bms = sum(bw["ms"]) / len(bw["ms"])
+        btf = bw["flops"] / (bms * 1e-3) / 1e12
+        result["backward"] = {
+            "workload": f"{w.name}: one rank's backward (dQ of its shard, its dK/dV share over the full K/V)",
+            "value": round(btf, 2), "unit": "TFLOP/s", "ms_per_rank_avg": round(bms, 3),
+            "per_rank_ms": {str(r): round(t, 3) for r, t in enumerate(bw["ms"])},
+            "roofline": {"bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(btf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": profiled_traffic("attn_bwd_bf16_llama70b_s131072_cp8.md",
+                                                     ("attn_bwd.hip", "attn_tiles.h", "common.h")),
+                         "traffic_unit": "HBM bytes per call (prep + dq + dkdv)",
+                         "kernel": "cp_attention_bwd call (bwd_delta + attn_bwd_dq + attn_bwd_dkdv)",
+                         "useful_flop_per_call": bw["flops"]}}
     if not args.no_decode:
         dw = synth.MIXTRAL_8X22B_DECODE
         d = bench_decode(dw, args.decode_iters, dev)

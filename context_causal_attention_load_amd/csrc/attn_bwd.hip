@@ -316,6 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
 constexpr int kKvWaves = 4;
 constexpr int kKvThreads = kKvWaves * 64;
 constexpr int kBKV = kKvWaves * 32;  // keys per workgroup
+constexpr int kKvStages = 3;         // LDS ring: a stage's copy is issued two stages ahead
 
 template <int DQK, int DV>
 struct DkvCfg {
@@ -342,10 +343,19 @@ struct DkvParams {
   const __bf16* v;
 };
 
+// A workgroup-uniform int from global memory through the scalar cache (a read, waited with
+// lgkmcnt). A plain load here would be a vector load whose vmcnt wait also drains the LDS copies
+// in flight.
+__device__ __forceinline__ int load_uniform_i32(const int* ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+
 template <int DQK, int DV>
 __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(DkvParams p, BwdExtra e) {
   using C = DkvCfg<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) char lds[kKvStages * C::STAGE];
 
   // work item: (b, g, chunk i, tile t). Each XCD takes a contiguous range of items, in which
   // tiles and chunks vary fastest, so an XCD holds whole kv heads (equal work) and its L2 serves
@@ -402,7 +412,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(DkvParams 
   const int* blkmin = e.blk;
   const int* blkmax = e.blk + e.nqb;
   auto next_visible = [&](int qb) {
-    while (qb < e.nqb && blkmax[qb] < kpos0) ++qb;
+    while (qb < e.nqb && load_uniform_i32(blkmax + qb) < kpos0) ++qb;
     return qb;
   };
 
@@ -434,16 +444,24 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(DkvParams 
       const unsigned off = (unsigned)(min(row, last) * o_row_bytes) + (unsigned)((phys ^ swz<C::OCH>(row)) * 16);
       dma16_sv(ot, off, ol + (u * kKvWaves + wave) * 1024);
     }
-    // log2-LSE, D and positions of the block's 32 rows: 3 x 128 bytes, 8 lanes each
-    if (wave == 0 && lane < 24) {
-      const int which = lane / 8, part = lane % 8;
+    // log2-LSE, D and positions of the block's 32 rows (128 bytes each): waves 0, 1, 2 copy one
+    // array each with 8 lanes
+    if (wave < 3) {
       const int64_t sidx = ((int64_t)b * p.Hq + h) * e.Sqp + qb * kBQ;
-      const char* src = which == 0 ? reinterpret_cast<const char*>(e.lse2 + sidx)
-                                   : (which == 1 ? reinterpret_cast<const char*>(e.delta + sidx)
-                                                 : reinterpret_cast<const char*>(e.pos + qb * kBQ));
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src + part * 16),
-                   "s"(__builtin_amdgcn_readfirstlane(sl)) : "memory", "m0");
+      const char* src = wave == 0 ? reinterpret_cast<const char*>(e.lse2 + sidx)
+                                  : (wave == 1 ? reinterpret_cast<const char*>(e.delta + sidx)
+                                               : reinterpret_cast<const char*>(e.pos + qb * kBQ));
+      if (lane < 8)
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src + lane * 16),
+                     "s"(sl + wave * 128) : "memory", "m0");
     }
+  };
+  // wait until at most one stage's copies (this wave's) are still in flight
+  auto wait_all_but_one_stage = [&]() {
+    if (wave < 3)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA + 1) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA) : "memory");
   };
 
   const int grp = lane / 16;
@@ -451,26 +469,84 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(DkvParams 
   const int tr_q = lane % 4;
   const int kpos = kpos0 + kk;
 
+  // stage sequence: (query block, head of the group), heads fastest; qb == nqb marks the end
+  auto advance = [&](int& sqb, int& sh) {
+    if (sqb >= e.nqb) return;
+    if (++sh == p.G) {
+      sh = 0;
+      sqb = next_visible(sqb + 1);
+    }
+  };
   int qb = next_visible(0), h = 0;
-  if (qb < e.nqb) {
-    dma_stage(qb, g * p.G, 0);
+  int qb1 = qb, h1 = h;
+  advance(qb1, h1);
+  if (qb < e.nqb) dma_stage(qb, g * p.G + h, 0);
+  if (qb1 < e.nqb) {
+    dma_stage(qb1, g * p.G + h1, 1);
+    wait_all_but_one_stage();
+  } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
   int buf = 0;
   while (qb < e.nqb) {
-    int nqb = qb, nh = h + 1;
-    if (nh == p.G) {
-      nh = 0;
-      nqb = next_visible(qb + 1);
-    }
-    if (nqb < e.nqb) dma_stage(nqb, g * p.G + nh, buf ^ 1);
+    int qb2 = qb1, h2 = h1;
+    advance(qb2, h2);
+    const int buf2 = buf >= kKvStages - 2 ? buf + 2 - kKvStages : buf + 2;
+    if (qb2 < e.nqb) dma_stage(qb2, g * p.G + h2, buf2);  // that slot was last read two stages ago
 
     const char* qt = lds + buf * C::STAGE;
     const char* ot = qt + C::Q_BYTES;
     const float* st_lse = reinterpret_cast<const float*>(ot + C::O_BYTES);
     const float* st_dlt = st_lse + kBQ;
     const int* st_pos = reinterpret_cast<const int*>(st_dlt + kBQ);
+
+    // every LDS fragment of the stage is read up front (one wave per SIMD leaves the registers
+    // for it), so the MFMAs below do not wait on LDS latency: rows of Q and dO (A operands of
+    // S and dP) and the transposing reads of dO and Q (A operands of dV^T and dK^T)
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    bf16x8 qa[C::QK_STEPS], oa[C::DV_STEPS];
+    {
+      const int row = lane & 31;
+      const char* qr = qt + row * (C::QCH * 16);
+      const int swq = swz<C::QCH>(row);
+#pragma unroll
+      for (int ks = 0; ks < C::QK_STEPS; ++ks)
+        qa[ks] = *reinterpret_cast<const bf16x8*>(qr + (((2 * ks + hl) ^ swq) * 16));
+      const char* orow = ot + row * (C::OCH * 16);
+      const int swo = swz<C::OCH>(row);
+#pragma unroll
+      for (int ks = 0; ks < C::DV_STEPS; ++ks)
+        oa[ks] = *reinterpret_cast<const bf16x8*>(orow + (((2 * ks + hl) ^ swo) * 16));
+    }
+    bf16x8 ot_a[2][C::MV], qt_a[2][C::MK];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int row_a = 16 * ks + 4 * (grp / 2) + tr_e;
+      const int row_b = row_a + 8;
+#pragma unroll
+      for (int m = 0; m < C::MV; ++m) {
+        const int col = 32 * m + 16 * (grp % 2) + 4 * tr_q;
+        const int ch = col / 8, within = (col % 8) * 2;
+        const char* pa = ot + row_a * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_a)) * 16) + within;
+        const char* pb2 = ot + row_b * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_b)) * 16) + within;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
+        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        ot_a[ks][m] = __builtin_bit_cast(bf16x8, cat);
+      }
+#pragma unroll
+      for (int m = 0; m < C::MK; ++m) {
+        const int col = 32 * m + 16 * (grp % 2) + 4 * tr_q;
+        const int ch = col / 8, within = (col % 8) * 2;
+        const char* pa = qt + row_a * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_a)) * 16) + within;
+        const char* pb2 = qt + row_b * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_b)) * 16) + within;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
+        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        qt_a[ks][m] = __builtin_bit_cast(bf16x8, cat);
+      }
+    }
 
     // seeds: -log2 LSE and -D of the rows this lane's outputs hold (rows 8 i + 4 hl + j)
     f32x16 sacc, dacc;
@@ -484,26 +560,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(DkvParams 
         dacc[4 * i + j] = -d4[j];
       }
     }
-    // S = Q K'^T - LSE and dP - D = dO V^T - D: A operands are rows of the Q / dO tiles
-    {
-      const int row = lane & 31;
-      const char* qr = qt + row * (C::QCH * 16);
-      const int swq = swz<C::QCH>(row);
+    // S = Q K'^T - LSE and dP - D = dO V^T - D, the two independent chains interleaved
 #pragma unroll
-      for (int ks = 0; ks < C::QK_STEPS; ++ks) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + (((2 * ks + hl) ^ swq) * 16));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
-      }
-      const char* orow = ot + row * (C::OCH * 16);
-      const int swo = swz<C::OCH>(row);
-#pragma unroll
-      for (int ks = 0; ks < C::DV_STEPS; ++ks) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + (((2 * ks + hl) ^ swo) * 16));
-        dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dacc, 0, 0, 0);
-      }
+    for (int ks = 0; ks < (C::QK_STEPS > C::DV_STEPS ? C::QK_STEPS : C::DV_STEPS); ++ks) {
+      if (ks < C::QK_STEPS) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], sacc, 0, 0, 0);
+      if (ks < C::DV_STEPS) dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[ks], vf[ks], dacc, 0, 0, 0);
     }
     // mask where a row does not see the key (or the key is past the tile's valid keys)
-    const bool need_mask = blkmin[qb] < kpos0 + kBKV - 1 || nvalid < kBKV || (qb + 1) * kBQ > p.Sq;
+    const bool need_mask = load_uniform_i32(blkmin + qb) < kpos0 + kBKV - 1 || nvalid < kBKV || (qb + 1) * kBQ > p.Sq;
     if (need_mask) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -522,44 +586,28 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(DkvParams 
       pb[r / 8][r % 8] = (__bf16)pr;
       dsb[r / 8][r % 8] = (__bf16)(pr * dacc[r]);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS, A operands from transposing reads of the tiles
+    // dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int row_a = 16 * ks + 4 * (grp / 2) + tr_e;
-      const int row_b = row_a + 8;
 #pragma unroll
-      for (int m = 0; m < C::MV; ++m) {
-        const int col = 32 * m + 16 * (grp % 2) + 4 * tr_q;
-        const int ch = col / 8, within = (col % 8) * 2;
-        const char* pa = ot + row_a * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_a)) * 16) + within;
-        const char* pb2 = ot + row_b * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_b)) * 16) + within;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
-        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[ks], dvacc[m], 0, 0,
-                                                           0);
-      }
+      for (int m = 0; m < C::MV; ++m)
+        dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot_a[ks][m], pb[ks], dvacc[m], 0, 0, 0);
 #pragma unroll
-      for (int m = 0; m < C::MK; ++m) {
-        const int col = 32 * m + 16 * (grp % 2) + 4 * tr_q;
-        const int ch = col / 8, within = (col % 8) * 2;
-        const char* pa = qt + row_a * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_a)) * 16) + within;
-        const char* pb2 = qt + row_b * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_b)) * 16) + within;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
-        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), dsb[ks], dkacc[m], 0, 0,
-                                                           0);
-      }
+      for (int m = 0; m < C::MK; ++m)
+        dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt_a[ks][m], dsb[ks], dkacc[m], 0, 0, 0);
     }
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the next stage's copies must have landed; the one after may stay in flight
+    if (qb2 < e.nqb)
+      wait_all_but_one_stage();
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    buf ^= 1;
-    qb = nqb;
-    h = nh;
+    buf = buf + 1 == kKvStages ? 0 : buf + 1;
+    qb = qb1;
+    h = h1;
+    qb1 = qb2;
+    h1 = h2;
   }
 
   // dK = scale dK^T, dV; lane holds key kk, dims 32 m + 8 a4 + 4 hl + t

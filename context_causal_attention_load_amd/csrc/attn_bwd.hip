@@ -353,7 +353,7 @@ __device__ __forceinline__ int load_uniform_i32(const int* ptr) {
 }
 
 template <int DQK, int DV>
-__global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(DkvParams p, BwdExtra e) {
+__global__ __launch_bounds__(kKvThreads, 2) void attn_bwd_dkdv_kernel(DkvParams p, BwdExtra e) {
   using C = DkvCfg<DQK, DV>;
   __shared__ __attribute__((aligned(16))) char lds[kKvStages * C::STAGE];
 
@@ -501,77 +501,50 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(DkvParams 
     const float* st_dlt = st_lse + kBQ;
     const int* st_pos = reinterpret_cast<const int*>(st_dlt + kBQ);
 
-    // every LDS fragment of the stage is read up front (one wave per SIMD leaves the registers
-    // for it), so the MFMAs below do not wait on LDS latency: rows of Q and dO (A operands of
-    // S and dP) and the transposing reads of dO and Q (A operands of dV^T and dK^T)
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    bf16x8 qa[C::QK_STEPS], oa[C::DV_STEPS];
-    {
-      const int row = lane & 31;
-      const char* qr = qt + row * (C::QCH * 16);
-      const int swq = swz<C::QCH>(row);
-#pragma unroll
-      for (int ks = 0; ks < C::QK_STEPS; ++ks)
-        qa[ks] = *reinterpret_cast<const bf16x8*>(qr + (((2 * ks + hl) ^ swq) * 16));
-      const char* orow = ot + row * (C::OCH * 16);
-      const int swo = swz<C::OCH>(row);
-#pragma unroll
-      for (int ks = 0; ks < C::DV_STEPS; ++ks)
-        oa[ks] = *reinterpret_cast<const bf16x8*>(orow + (((2 * ks + hl) ^ swo) * 16));
-    }
-    bf16x8 ot_a[2][C::MV], qt_a[2][C::MK];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int row_a = 16 * ks + 4 * (grp / 2) + tr_e;
-      const int row_b = row_a + 8;
-#pragma unroll
-      for (int m = 0; m < C::MV; ++m) {
-        const int col = 32 * m + 16 * (grp % 2) + 4 * tr_q;
-        const int ch = col / 8, within = (col % 8) * 2;
-        const char* pa = ot + row_a * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_a)) * 16) + within;
-        const char* pb2 = ot + row_b * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_b)) * 16) + within;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
-        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        ot_a[ks][m] = __builtin_bit_cast(bf16x8, cat);
-      }
-#pragma unroll
-      for (int m = 0; m < C::MK; ++m) {
-        const int col = 32 * m + 16 * (grp % 2) + 4 * tr_q;
-        const int ch = col / 8, within = (col % 8) * 2;
-        const char* pa = qt + row_a * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_a)) * 16) + within;
-        const char* pb2 = qt + row_b * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_b)) * 16) + within;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
-        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        qt_a[ks][m] = __builtin_bit_cast(bf16x8, cat);
-      }
-    }
+    // Lane-dependent LDS offsets are recomputed from an opaque copy of the lane index in every
+    // stage: hoisted out of the loop they would hold ~40 registers and push the kernel past the
+    // 256 that two waves per SIMD allow.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int row = ln & 31, lhl = ln >> 5, lgrp = ln >> 4;
+    const int ltr_e = (ln & 15) >> 2, ltr_q = ln & 3;
 
     // seeds: -log2 LSE and -D of the rows this lane's outputs hold (rows 8 i + 4 hl + j)
     f32x16 sacc, dacc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(st_lse + 8 * i + 4 * hl);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st_dlt + 8 * i + 4 * hl);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(st_lse + 8 * i + 4 * lhl);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st_dlt + 8 * i + 4 * lhl);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         sacc[4 * i + j] = -l4[j];
         dacc[4 * i + j] = -d4[j];
       }
     }
-    // S = Q K'^T - LSE and dP - D = dO V^T - D, the two independent chains interleaved
+    // S = Q K'^T - LSE and dP - D = dO V^T - D: A operands are rows of the Q / dO tiles
+    {
+      const char* qr = qt + row * (C::QCH * 16);
+      const int swq = swz<C::QCH>(row);
+      const char* orow = ot + row * (C::OCH * 16);
+      const int swo = swz<C::OCH>(row);
 #pragma unroll
-    for (int ks = 0; ks < (C::QK_STEPS > C::DV_STEPS ? C::QK_STEPS : C::DV_STEPS); ++ks) {
-      if (ks < C::QK_STEPS) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], sacc, 0, 0, 0);
-      if (ks < C::DV_STEPS) dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[ks], vf[ks], dacc, 0, 0, 0);
+      for (int ks = 0; ks < (C::QK_STEPS > C::DV_STEPS ? C::QK_STEPS : C::DV_STEPS); ++ks) {
+        if (ks < C::QK_STEPS) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + (((2 * ks + lhl) ^ swq) * 16));
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
+        }
+        if (ks < C::DV_STEPS) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + (((2 * ks + lhl) ^ swo) * 16));
+          dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dacc, 0, 0, 0);
+        }
+      }
     }
     // mask where a row does not see the key (or the key is past the tile's valid keys)
     const bool need_mask = load_uniform_i32(blkmin + qb) < kpos0 + kBKV - 1 || nvalid < kBKV || (qb + 1) * kBQ > p.Sq;
     if (need_mask) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int4 q4 = *reinterpret_cast<const int4*>(st_pos + 8 * i + 4 * hl);
+        const int4 q4 = *reinterpret_cast<const int4*>(st_pos + 8 * i + 4 * lhl);
         const int qp[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) sacc[4 * i + j] = (kk < nvalid && kpos <= qp[j]) ? sacc[4 * i + j] : -INFINITY;
@@ -586,15 +559,36 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(DkvParams 
       pb[r / 8][r % 8] = (__bf16)pr;
       dsb[r / 8][r % 8] = (__bf16)(pr * dacc[r]);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS
+    // dV^T += dO^T P and dK^T += Q^T dS, A operands from transposing reads of the tiles
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      const int row_a = 16 * ks + 4 * (lgrp / 2) + ltr_e;
+      const int row_b = row_a + 8;
 #pragma unroll
-      for (int m = 0; m < C::MV; ++m)
-        dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot_a[ks][m], pb[ks], dvacc[m], 0, 0, 0);
+      for (int m = 0; m < C::MV; ++m) {
+        const int col = 32 * m + 16 * (lgrp % 2) + 4 * ltr_q;
+        const int ch = col / 8, within = (col % 8) * 2;
+        const char* pa = ot + row_a * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_a)) * 16) + within;
+        const char* pb2 = ot + row_b * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_b)) * 16) + within;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
+        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[ks], dvacc[m], 0, 0,
+                                                           0);
+      }
 #pragma unroll
-      for (int m = 0; m < C::MK; ++m)
-        dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt_a[ks][m], dsb[ks], dkacc[m], 0, 0, 0);
+      for (int m = 0; m < C::MK; ++m) {
+        const int col = 32 * m + 16 * (lgrp % 2) + 4 * ltr_q;
+        const int ch = col / 8, within = (col % 8) * 2;
+        const char* pa = qt + row_a * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_a)) * 16) + within;
+        const char* pb2 = qt + row_b * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_b)) * 16) + within;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
+        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), dsb[ks], dkacc[m], 0, 0,
+                                                           0);
+      }
     }
 
     // the next stage's copies must have landed; the one after may stay in flight

@@ -211,9 +211,9 @@ int cp_attention_bwd(const void* q_shard, const void* k, const void* v, const vo
   if (!q_positions && sq != seq / cp)
     return fail(CPA_EINVAL, "%s: without q_positions, sq (%d) must equal seq/cp (%d)", where, sq, seq / cp);
   if (dtype != CPA_F32 && dtype != CPA_BF16) return fail(CPA_EINVAL, "%s: unknown dtype %d", where, dtype);
-  if (dtype != CPA_BF16 || !((d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128)))
-    return fail(CPA_ENOTSUP, "%s: (dtype %d, d_qk %d, d_v %d) not supported (bf16 with 64/64 or 128/128)", where,
-                dtype, d_qk, d_v);
+  if (dtype != CPA_BF16 || !((d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128)))
+    return fail(CPA_ENOTSUP, "%s: (dtype %d, d_qk %d, d_v %d) not supported (bf16 with 64/64, 128/128, 192/128)",
+                where, dtype, d_qk, d_v);
   if ((int64_t)batch * seq * hkv * d_qk * 4 >= (int64_t(1) << 40) ||
       (int64_t)batch * sq * hq * d_qk * 4 >= (int64_t(1) << 40) || (int64_t)hq * d_qk * 2 * 32 >= (int64_t(1) << 31))
     return fail(CPA_EINVAL, "%s: tensor too large", where);

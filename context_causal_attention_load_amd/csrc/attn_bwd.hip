@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
   // Q fragment (scaled, B operand of S^T = K Q'^T) and dO fragment (B operand of V dO^T):
   // lane holds row (lane & 31), dims 16 ks + 8 hl .. + 7
   bf16x8 qf[C::QK_STEPS], df[C::DV_STEPS];
-  f32x16 c_lse, c_dlt;
+  float neg_l2, neg_d;  // -log2 LSE and -D of the lane's row: the seeds of the two products
   {
     const int row = my_row < p.Sq ? my_row : p.Sq - 1;
     const bf16x8* qrow = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.q) +
@@ -155,17 +155,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
 #pragma unroll
     for (int ks = 0; ks < C::DV_STEPS; ++ks) df[ks] = drow[2 * ks + hl];
     const int64_t sidx = ((int64_t)w.b * p.Hq + head) * e.Sqp + row;
-    const float l2 = e.lse2[sidx], dl = e.delta[sidx];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      c_lse[r] = -l2;
-      c_dlt[r] = -dl;
-    }
+    neg_l2 = -e.lse2[sidx];
+    neg_d = -e.delta[sidx];
 #pragma unroll
     for (int ks = 0; ks < C::QK_STEPS; ++ks) asm volatile("" ::"v"(qf[ks]));
 #pragma unroll
     for (int ks = 0; ks < C::DV_STEPS; ++ks) asm volatile("" ::"v"(df[ks]));
-    asm volatile("" ::"v"(c_lse), "v"(c_dlt));
+    asm volatile("" ::"v"(neg_l2), "v"(neg_d));
   }
 
   const int64_t kv_row_bytes_k = (int64_t)p.Hkv * DQK * 2;
@@ -211,15 +207,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
   f32x16 dqacc[C::MQ];
 #pragma unroll
   for (int m = 0; m < C::MQ; ++m) dqacc[m] = f32x16{};
+  // the MFMA seeds as full vectors (32 registers, read in place by the products)
+  f32x16 seed_l, seed_d;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    seed_l[r] = neg_l2;
+    seed_d[r] = neg_d;
+  }
 
   TileCursor tc{0, 0};
   dma_tile(tc, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int buf = 0;
-  const int grp = lane / 16;
-  const int tr_e = (lane % 16) / 4;
-  const int tr_q = lane % 4;
 
   while (tc.chunk <= imax) {
     TileCursor nx = tc;
@@ -235,26 +235,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
     const bool need_mask = (kpos0 + C::BK - 1 > qmin) || (nvalid < C::BK);
     // key kk of the tile is visible iff kk <= lim (kk < nvalid and kpos0 + kk <= my_pos)
     const int lim = min(nvalid - 1, my_pos - kpos0) - 4 * hl;
+    // for Dqk > 128, lane-dependent LDS offsets come from an opaque copy of the lane index and
+    // are recomputed per tile: hoisted out of the loop they would cost registers that the wider
+    // head dims do not have (for smaller dims hoisting is cheaper)
+    int ln = lane;
+    if constexpr (DQK > 128) asm volatile("" : "+v"(ln));  // only the widest head dims need it
+    const int lhl = ln >> 5, lgrp = ln >> 4, ltr_e = (ln & 15) >> 2, ltr_q = ln & 3;
 
     // one 32-key block at a time: exponents of P (S^T = K Q'^T - LSE), dP^T - D = V dO^T - D,
     // dS^T rounded to bf16, then its two k-steps of dQ^T += K^T dS^T
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
-      const int krow = mb * 32 + (lane & 31);
-      f32x16 sacc = c_lse;
+      const int krow = mb * 32 + (ln & 31);
+      f32x16 sacc = seed_l, dacc = seed_d;
       const char* kr = kb + krow * (C::KCH * 16);
       const int swk = swz<C::KCH>(krow);
 #pragma unroll
       for (int ks = 0; ks < C::QK_STEPS; ++ks) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + (((2 * ks + hl) ^ swk) * 16));
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + (((2 * ks + lhl) ^ swk) * 16));
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc, 0, 0, 0);
       }
-      f32x16 dacc = c_dlt;
       const char* vr = vb + krow * (C::VCH * 16);
       const int swv = swz<C::VCH>(krow);
 #pragma unroll
       for (int ks = 0; ks < C::DV_STEPS; ++ks) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(vr + (((2 * ks + hl) ^ swv) * 16));
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(vr + (((2 * ks + lhl) ^ swv) * 16));
         dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[ks], dacc, 0, 0, 0);
       }
       if (need_mask) {
@@ -271,11 +276,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int ks = 2 * mb + j;
-        const int row_a = 16 * ks + 4 * (grp / 2) + tr_e;
+        const int row_a = 16 * ks + 4 * (lgrp / 2) + ltr_e;
         const int row_b = row_a + 8;
 #pragma unroll
         for (int m = 0; m < C::MQ; ++m) {
-          const int col = 32 * m + 16 * (grp % 2) + 4 * tr_q;
+          const int col = 32 * m + 16 * (lgrp % 2) + 4 * ltr_q;
           const int ch = col / 8, within = (col % 8) * 2;
           const char* pa = kb + row_a * (C::KCH * 16) + ((ch ^ swz<C::KCH>(row_a)) * 16) + within;
           const char* pb2 = kb + row_b * (C::KCH * 16) + ((ch ^ swz<C::KCH>(row_b)) * 16) + within;
@@ -353,7 +358,7 @@ __device__ __forceinline__ int load_uniform_i32(const int* ptr) {
 }
 
 template <int DQK, int DV>
-__global__ __launch_bounds__(kKvThreads, 2) void attn_bwd_dkdv_kernel(DkvParams p, BwdExtra e) {
+__global__ __launch_bounds__(kKvThreads, DQK > 128 ? 1 : 2) void attn_bwd_dkdv_kernel(DkvParams p, BwdExtra e) {
   using C = DkvCfg<DQK, DV>;
   __shared__ __attribute__((aligned(16))) char lds[kKvStages * C::STAGE];
 
@@ -706,6 +711,7 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   if (a.batch == 0 || a.sq == 0) return hipSuccess;
   if (a.d_qk == 128 && a.d_v == 128) return launch_bwd_typed<128, 128>(a, stream);
   if (a.d_qk == 64 && a.d_v == 64) return launch_bwd_typed<64, 64>(a, stream);
+  if (a.d_qk == 192 && a.d_v == 128) return launch_bwd_typed<192, 128>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -148,7 +148,7 @@ int cp_attention_fwd(const void* q_shard, const void* k, const void* v,
  *   workspace, workspace_bytes: at least cp_attention_bwd_workspace_bytes(batch, sq, hq) bytes of
  *            caller-owned device scratch; contents on entry do not matter; calls sharing one
  *            workspace must not overlap.
- * Supported: bf16 with (d_qk, d_v) in {(64, 64), (128, 128)}; CPA_ENOTSUP otherwise. CPA_EINVAL
+ * Supported: bf16 with (d_qk, d_v) in {(64, 64), (128, 128), (192, 128)}; CPA_ENOTSUP otherwise. CPA_EINVAL
  * for the forward's argument errors, null pointers (all tensors are required), tensors not
  * 16-byte aligned (lse and q_positions: 4-byte), or a workspace that is too small. */
 size_t cp_attention_bwd_workspace_bytes(int32_t batch, int32_t sq, int32_t hq);

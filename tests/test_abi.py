@@ -149,7 +149,7 @@ def _bwd(lib, **kw):
     (dict(scale=-0.5), binding.CPA_EINVAL, "softmax_scale"),
     (dict(sq=100), binding.CPA_EINVAL, "without q_positions"),
     (dict(dtype=binding.CPA_F32), binding.CPA_ENOTSUP, "not supported"),
-    (dict(dqk=192, dv_=128), binding.CPA_ENOTSUP, "not supported"),
+    (dict(dqk=96, dv_=96), binding.CPA_ENOTSUP, "not supported"),
     (dict(dtype=5), binding.CPA_EINVAL, "dtype"),
     (dict(lse=None), binding.CPA_EINVAL, "null"),
     (dict(dk=ctypes.c_void_p(4100)), binding.CPA_EINVAL, "aligned"),

@@ -542,9 +542,10 @@ def run_bwd_rank(qd, kd, vd, dod, seq, cp, rank, scale, kp=None, vp=None):
     return dq, dk, dv
 
 
-def check_bwd_full(batch, seq, cp, hq, hkv, d, ranks, seed, tag):
-    q, k, v = synth.prefill_inputs(batch, seq, hq, hkv, d, d, torch.bfloat16, seed)
-    do = synth.prefill_grad(batch, seq, hq, d, torch.bfloat16, seed + 1000)
+def check_bwd_full(batch, seq, cp, hq, hkv, d, ranks, seed, tag, d_v=None):
+    d_v = d if d_v is None else d_v
+    q, k, v = synth.prefill_inputs(batch, seq, hq, hkv, d, d_v, torch.bfloat16, seed)
+    do = synth.prefill_grad(batch, seq, hq, d_v, torch.bfloat16, seed + 1000)
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
     kp, vp = cpa.permute(kd, cp), cpa.permute(vd, cp)
     perm = olb.load_balance_perm(seq, cp)
@@ -571,6 +572,11 @@ def test_backward_small(batch, seq, cp, hq, hkv, d, ranks):
     check_bwd_full(batch, seq, cp, hq, hkv, d, ranks, seed=seq + hq, tag=f"B{batch} S{seq} Hq{hq}/{hkv} D{d}")
 
 
+def test_backward_mla_shape_small():
+    """MLA-style head dims (q/k 192 = 128 + 64 rotary, v 128) at a small size, both ranks."""
+    check_bwd_full(1, 768, 2, 4, 4, 192, (0, 1), seed=23, tag="MLA Dqk192 Dv128", d_v=128)
+
+
 def test_backward_contiguous_shard_positions():
     """Explicit q_positions: a contiguous (unbalanced) shard of the natural order, K/V natural."""
     seq, hq, hkv, d = 512, 4, 2, 64
@@ -595,14 +601,12 @@ def test_backward_llama7b_s8192():
     check_bwd_full(w.batch, w.seq, 4, w.hq, w.hkv, w.d_qk, (0, 3), seed=w.seed, tag=w.name)
 
 
-@pytest.mark.parametrize("rank", [0, 7])
-def test_backward_llama70b_full_size_sampled(rank):
-    """131072 tokens, cp = 8, one rank at its real shape. dQ on sampled rows; dK, dV at the keys
-    of the last 48 positions of the rank's upper chunk (seen only by the rank's rows at those
-    positions, all of which are in the sample); keys past the rank's last position are exactly
-    0; and dK sums to ~0 over the keys of each kv head (the softmax gradient sums to zero)."""
-    w = synth.LLAMA31_70B_S131K
-    cp, S = 8, w.seq
+def sampled_bwd_check(w, cp, rank):
+    """One rank at its real shape. dQ on sampled rows; dK, dV at the keys of the last 48
+    positions of the rank's upper chunk (seen only by the rank's rows at those positions, all of
+    which are in the sample); keys past the rank's last position are exactly 0; and dK sums to ~0
+    over the keys of each kv head (the softmax gradient sums to zero)."""
+    S = w.seq
     c = S // (2 * cp)
     announce(f"backward {w.name} rank {rank} (sampled)")
     q, k, v = synth.workload_prefill_inputs(w)
@@ -629,3 +633,13 @@ def test_backward_llama70b_full_size_sampled(rank):
     scale_ref = dk.abs().sum(dim=1).max().item()
     print(f"  sum_j dK_j: max |.| {ssum:.3e} against max sum_j |dK_j| {scale_ref:.3e}", flush=True)
     assert ssum <= 1e-2 * scale_ref
+
+
+@pytest.mark.parametrize("rank", [0, 3])
+def test_backward_deepseek_mla_full_size_sampled(rank):
+    sampled_bwd_check(synth.DEEPSEEK_V3_MLA_S32K, 4, rank)
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_backward_llama70b_full_size_sampled(rank):
+    sampled_bwd_check(synth.LLAMA31_70B_S131K, 8, rank)

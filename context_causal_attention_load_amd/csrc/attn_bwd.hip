@@ -543,6 +543,14 @@ __global__ __launch_bounds__(kKvThreads, DQK > 128 ? 1 : 2) void attn_bwd_dkdv_k
           dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dacc, 0, 0, 0);
         }
       }
+      // keep each row-fragment read two MFMAs ahead of its use
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < C::QK_STEPS + C::DV_STEPS - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     // mask where a row does not see the key (or the key is past the tile's valid keys)
     const bool need_mask = load_uniform_i32(blkmin + qb) < kpos0 + kBKV - 1 || nvalid < kBKV || (qb + 1) * kBQ > p.Sq;
@@ -566,16 +574,17 @@ __global__ __launch_bounds__(kKvThreads, DQK > 128 ? 1 : 2) void attn_bwd_dkdv_k
     }
     // dV^T += dO^T P and dK^T += Q^T dS, A operands from transposing reads of the tiles
     typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const unsigned cbase = 16u * (unsigned)(lgrp & 1) + 4u * (unsigned)ltr_q;  // column within a 32-block
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int row_a = 16 * ks + 4 * (lgrp / 2) + ltr_e;
+      const int row_a = 16 * ks + 4 * (lgrp >> 1) + ltr_e;
       const int row_b = row_a + 8;
 #pragma unroll
       for (int m = 0; m < C::MV; ++m) {
-        const int col = 32 * m + 16 * (lgrp % 2) + 4 * ltr_q;
-        const int ch = col / 8, within = (col % 8) * 2;
-        const char* pa = ot + row_a * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_a)) * 16) + within;
-        const char* pb2 = ot + row_b * (C::OCH * 16) + ((ch ^ swz<C::OCH>(row_b)) * 16) + within;
+        const unsigned col = 32u * m + cbase;
+        const unsigned ch = col >> 3, within = (col & 7u) * 2u;
+        const char* pa = ot + row_a * (C::OCH * 16) + ((ch ^ (unsigned)swz<C::OCH>(row_a)) * 16u) + within;
+        const char* pb2 = ot + row_b * (C::OCH * 16) + ((ch ^ (unsigned)swz<C::OCH>(row_b)) * 16u) + within;
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
         i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -584,10 +593,10 @@ __global__ __launch_bounds__(kKvThreads, DQK > 128 ? 1 : 2) void attn_bwd_dkdv_k
       }
 #pragma unroll
       for (int m = 0; m < C::MK; ++m) {
-        const int col = 32 * m + 16 * (lgrp % 2) + 4 * ltr_q;
-        const int ch = col / 8, within = (col % 8) * 2;
-        const char* pa = qt + row_a * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_a)) * 16) + within;
-        const char* pb2 = qt + row_b * (C::QCH * 16) + ((ch ^ swz<C::QCH>(row_b)) * 16) + within;
+        const unsigned col = 32u * m + cbase;
+        const unsigned ch = col >> 3, within = (col & 7u) * 2u;
+        const char* pa = qt + row_a * (C::QCH * 16) + ((ch ^ (unsigned)swz<C::QCH>(row_a)) * 16u) + within;
+        const char* pb2 = qt + row_b * (C::QCH * 16) + ((ch ^ (unsigned)swz<C::QCH>(row_b)) * 16u) + within;
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
         i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -595,6 +604,14 @@ __global__ __launch_bounds__(kKvThreads, DQK > 128 ? 1 : 2) void attn_bwd_dkdv_k
                                                            0);
       }
     }
+    // keep the transposing reads (two per MFMA) ahead of their MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * (C::MV + C::MK) - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
     // the next stage's copies must have landed; the one after may stay in flight
     if (qb2 < e.nqb)

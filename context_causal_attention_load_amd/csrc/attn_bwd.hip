@@ -18,9 +18,10 @@
 //    in original order). Per tile: S^T = K Q'^T seeded with -LSE (so the products are the
 //    exponents of P), dP^T - D = V dO^T seeded with -D, dS^T = P^T (dP^T - D) rounded to bf16,
 //    then dQ^T += K^T dS^T with K^T from the transposing LDS read (ds_read_b64_tr_b16).
-//  * dkdv: key-stationary. A workgroup owns 128 keys of one kv head (32 per wave); the keys'
-//    K' (scaled) and V fragments stay in registers as B operands. It streams (32-row query
-//    block, query head) stages of Q, dO, log2-LSE, D and positions through double-buffered LDS,
+//  * dkdv: key-stationary. A workgroup owns 32 keys per wave of one kv head (256 keys at
+//    Dqk = 128, else 128); the keys' K' (scaled) and V fragments stay in registers as B operands.
+//    It streams (32-row query block, query head) stages of Q, dO, log2-LSE, D and positions
+//    through a 3-stage LDS ring,
 //    skipping blocks whose rows are all before the keys. Per stage: S = Q K'^T seeded with
 //    -LSE, dP - D = dO V^T seeded with -D; P and dS come out with a lane per key, already in
 //    the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS, whose A operands are the
@@ -318,22 +319,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
 // ------------------------------------------------------------------------------------------
 // dkdv kernel
 // ------------------------------------------------------------------------------------------
-constexpr int kKvWaves = 4;
-constexpr int kKvThreads = kKvWaves * 64;
-constexpr int kBKV = kKvWaves * 32;  // keys per workgroup
-constexpr int kKvStages = 3;         // LDS ring: a stage's copy is issued two stages ahead
+constexpr int kKvStages = 3;  // LDS ring: a stage's copy is issued two stages ahead
+
+// Waves per workgroup of the dkdv kernel, 32 keys each. Every workgroup streams the Q and dO rows
+// that see its keys, so more keys per workgroup means fewer passes over that stream: 8 waves
+// (256 keys, one workgroup per CU) at Dqk = 128; 4 at Dqk = 64 (a stage is only four waves' worth
+// of copies) and at Dqk = 192 (one wave per SIMD holds its 342 registers).
+template <int DQK>
+struct KvShape {
+  static constexpr int WAVES = DQK == 128 ? 8 : 4;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int BKV = WAVES * 32;  // keys per workgroup
+  static constexpr int MIN_WG_PER_CU = (WAVES == 8 || DQK > 128) ? 1 : 2;
+};
 
 template <int DQK, int DV>
 struct DkvCfg {
+  static constexpr int WAVES = KvShape<DQK>::WAVES;
+  static constexpr int BKV = KvShape<DQK>::BKV;
   static constexpr int QCH = DQK / 8;
   static constexpr int OCH = DV / 8;
   static constexpr int Q_BYTES = kBQ * QCH * 16;
   static constexpr int O_BYTES = kBQ * OCH * 16;
   static constexpr int STAT_BYTES = 3 * kBQ * 4;  // log2-LSE, D, positions
   static constexpr int STAGE = Q_BYTES + O_BYTES + STAT_BYTES;
-  static constexpr int Q_DMA = Q_BYTES / (kKvWaves * 1024);
-  static constexpr int O_DMA = O_BYTES / (kKvWaves * 1024);
-  static_assert(Q_BYTES % (kKvWaves * 1024) == 0 && O_BYTES % (kKvWaves * 1024) == 0, "stage/wave mismatch");
+  static constexpr int Q_DMA = Q_BYTES / (WAVES * 1024);
+  static constexpr int O_DMA = O_BYTES / (WAVES * 1024);
+  static_assert(Q_BYTES % (WAVES * 1024) == 0 && O_BYTES % (WAVES * 1024) == 0, "stage/wave mismatch");
   static constexpr int QK_STEPS = DQK / 16;
   static constexpr int DV_STEPS = DV / 16;
   static constexpr int MK = DQK / 32;
@@ -358,7 +370,8 @@ __device__ __forceinline__ int load_uniform_i32(const int* ptr) {
 }
 
 template <int DQK, int DV>
-__global__ __launch_bounds__(kKvThreads, DQK > 128 ? 1 : 2) void attn_bwd_dkdv_kernel(DkvParams p, BwdExtra e) {
+__global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU) void attn_bwd_dkdv_kernel(
+    DkvParams p, BwdExtra e) {
   using C = DkvCfg<DQK, DV>;
   __shared__ __attribute__((aligned(16))) char lds[kKvStages * C::STAGE];
 
@@ -376,9 +389,9 @@ __global__ __launch_bounds__(kKvThreads, DQK > 128 ? 1 : 2) void attn_bwd_dkdv_k
   t /= 2 * p.cp;
   const int g = t % p.Hkv;
   const int b = t / p.Hkv;
-  const int t0 = tile * kBKV;
+  const int t0 = tile * C::BKV;
   const int kpos0 = chunk * p.c + t0;
-  const int nvalid = min(kBKV, p.c - t0);
+  const int nvalid = min(C::BKV, p.c - t0);
   const int64_t prow0 = lb_chunk_offset(chunk, p.c, p.cp) + t0;  // gathered slot of key 0
 
   const int tid = threadIdx.x;
@@ -427,7 +440,7 @@ __global__ __launch_bounds__(kKvThreads, DQK > 128 ? 1 : 2) void attn_bwd_dkdv_k
   const char* obase = reinterpret_cast<const char*>(e.dout) + (int64_t)b * p.Sq * o_row_bytes;
   const unsigned lds0 = (unsigned)(uintptr_t)lds;
   // per-lane DMA geometry: wave-instruction u of a stage fills LDS bytes
-  // [1024 (u * kKvWaves + wave), + 1024) of the Q (or dO) tile; lane l at + 16 l
+  // [1024 (u * C::WAVES + wave), + 1024) of the Q (or dO) tile; lane l at + 16 l
   auto dma_stage = [&](int qb, int h, int bufi) {
     const unsigned ql = lds0 + bufi * C::STAGE;
     const unsigned ol = ql + C::Q_BYTES;
@@ -437,17 +450,17 @@ __global__ __launch_bounds__(kKvThreads, DQK > 128 ? 1 : 2) void attn_bwd_dkdv_k
     const char* ot = obase + (int64_t)qb * kBQ * o_row_bytes + (int64_t)h * DV * 2;
 #pragma unroll
     for (int u = 0; u < C::Q_DMA; ++u) {
-      const int pos = (u * kKvWaves + wave) * 1024 + lane * 16;
+      const int pos = (u * C::WAVES + wave) * 1024 + lane * 16;
       const int row = pos / (C::QCH * 16), phys = (pos % (C::QCH * 16)) / 16;
       const unsigned off = (unsigned)(min(row, last) * q_row_bytes) + (unsigned)((phys ^ swz<C::QCH>(row)) * 16);
-      dma16_sv(qt, off, ql + (u * kKvWaves + wave) * 1024);
+      dma16_sv(qt, off, ql + (u * C::WAVES + wave) * 1024);
     }
 #pragma unroll
     for (int u = 0; u < C::O_DMA; ++u) {
-      const int pos = (u * kKvWaves + wave) * 1024 + lane * 16;
+      const int pos = (u * C::WAVES + wave) * 1024 + lane * 16;
       const int row = pos / (C::OCH * 16), phys = (pos % (C::OCH * 16)) / 16;
       const unsigned off = (unsigned)(min(row, last) * o_row_bytes) + (unsigned)((phys ^ swz<C::OCH>(row)) * 16);
-      dma16_sv(ot, off, ol + (u * kKvWaves + wave) * 1024);
+      dma16_sv(ot, off, ol + (u * C::WAVES + wave) * 1024);
     }
     // log2-LSE, D and positions of the block's 32 rows (128 bytes each): waves 0, 1, 2 copy one
     // array each with 8 lanes
@@ -553,7 +566,7 @@ __global__ __launch_bounds__(kKvThreads, DQK > 128 ? 1 : 2) void attn_bwd_dkdv_k
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     // mask where a row does not see the key (or the key is past the tile's valid keys)
-    const bool need_mask = load_uniform_i32(blkmin + qb) < kpos0 + kBKV - 1 || nvalid < kBKV || (qb + 1) * kBQ > p.Sq;
+    const bool need_mask = load_uniform_i32(blkmin + qb) < kpos0 + C::BKV - 1 || nvalid < C::BKV || (qb + 1) * kBQ > p.Sq;
     if (need_mask) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -706,14 +719,15 @@ hipError_t launch_bwd_typed(const AttnBwdArgs& a, hipStream_t stream) {
   d.G = a.hq / a.hkv;
   d.cp = a.cp;
   d.c = a.seq / (2 * a.cp);
-  d.ntc = (d.c + kBKV - 1) / kBKV;
+  d.ntc = (d.c + KvShape<DQK>::BKV - 1) / KvShape<DQK>::BKV;
   d.n_items = 2 * a.cp * d.B * d.Hkv * d.ntc;
   d.per_xcd = (d.n_items + kNumXcd - 1) / kNumXcd;
   d.scale_log2 = a.scale * kLog2e;
   d.q = static_cast<const __bf16*>(a.q);
   d.k = static_cast<const __bf16*>(a.k);
   d.v = static_cast<const __bf16*>(a.v);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV>), dim3(d.per_xcd * kNumXcd), dim3(kKvThreads), 0, stream, d, e);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV>), dim3(d.per_xcd * kNumXcd), dim3(KvShape<DQK>::THREADS), 0,
+                     stream, d, e);
   return hipGetLastError();
 }
 

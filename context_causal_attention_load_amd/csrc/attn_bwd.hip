@@ -545,14 +545,19 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
       const int swq = swz<C::QCH>(row);
       const char* orow = ot + row * (C::OCH * 16);
       const int swo = swz<C::OCH>(row);
+      // chunk (2 ks + hl) ^ sw = 2 ks ^ (hl ^ sw): one xor per k-step on a per-lane constant
+      const unsigned tq = (unsigned)(lhl ^ swq), to = (unsigned)(lhl ^ swo);
 #pragma unroll
       for (int ks = 0; ks < (C::QK_STEPS > C::DV_STEPS ? C::QK_STEPS : C::DV_STEPS); ++ks) {
         if (ks < C::QK_STEPS) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + (((2 * ks + lhl) ^ swq) * 16));
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + ((tq ^ (2u * ks)) << 4));
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
         }
         if (ks < C::DV_STEPS) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + (((2 * ks + lhl) ^ swo) * 16));
+          // with equal row layouts the dO tile's offsets are the Q tile's plus its size
+          const bf16x8 a = C::QCH == C::OCH
+                               ? *reinterpret_cast<const bf16x8*>(qr + ((tq ^ (2u * ks)) << 4) + C::Q_BYTES)
+                               : *reinterpret_cast<const bf16x8*>(orow + ((to ^ (2u * ks)) << 4));
           dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dacc, 0, 0, 0);
         }
       }
@@ -588,16 +593,19 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
     // dV^T += dO^T P and dK^T += Q^T dS, A operands from transposing reads of the tiles
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     const unsigned cbase = 16u * (unsigned)(lgrp & 1) + 4u * (unsigned)ltr_q;  // column within a 32-block
+    // Column block m adds 4 m to the 16-byte chunk, which only touches chunk bits 2..3, so
+    // (4 m + c) ^ sw = 4 m ^ (c ^ sw); rows 16 further (the next k-step) keep the swizzle.
+    const int row_a0 = 4 * (lgrp >> 1) + ltr_e, row_b0 = row_a0 + 8;
+    const unsigned c0 = cbase >> 3, within = (cbase & 7u) * 2u;
+    const unsigned ta = c0 ^ (unsigned)swz<C::OCH>(row_a0), tb = c0 ^ (unsigned)swz<C::OCH>(row_b0);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int row_a = 16 * ks + 4 * (lgrp >> 1) + ltr_e;
+      const int row_a = 16 * ks + row_a0;
       const int row_b = row_a + 8;
 #pragma unroll
       for (int m = 0; m < C::MV; ++m) {
-        const unsigned col = 32u * m + cbase;
-        const unsigned ch = col >> 3, within = (col & 7u) * 2u;
-        const char* pa = ot + row_a * (C::OCH * 16) + ((ch ^ (unsigned)swz<C::OCH>(row_a)) * 16u) + within;
-        const char* pb2 = ot + row_b * (C::OCH * 16) + ((ch ^ (unsigned)swz<C::OCH>(row_b)) * 16u) + within;
+        const char* pa = ot + row_a * (C::OCH * 16) + ((ta ^ (4u * m)) << 4) + within;
+        const char* pb2 = ot + row_b * (C::OCH * 16) + ((tb ^ (4u * m)) << 4) + within;
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
         i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -606,10 +614,10 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
       }
 #pragma unroll
       for (int m = 0; m < C::MK; ++m) {
-        const unsigned col = 32u * m + cbase;
-        const unsigned ch = col >> 3, within = (col & 7u) * 2u;
-        const char* pa = qt + row_a * (C::QCH * 16) + ((ch ^ (unsigned)swz<C::QCH>(row_a)) * 16u) + within;
-        const char* pb2 = qt + row_b * (C::QCH * 16) + ((ch ^ (unsigned)swz<C::QCH>(row_b)) * 16u) + within;
+        const unsigned qa = C::QCH == C::OCH ? ta : c0 ^ (unsigned)swz<C::QCH>(row_a0);
+        const unsigned qb_ = C::QCH == C::OCH ? tb : c0 ^ (unsigned)swz<C::QCH>(row_b0);
+        const char* pa = qt + row_a * (C::QCH * 16) + ((qa ^ (4u * m)) << 4) + within;
+        const char* pb2 = qt + row_b * (C::QCH * 16) + ((qb_ ^ (4u * m)) << 4) + within;
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
         i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};

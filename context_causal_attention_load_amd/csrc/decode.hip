@@ -206,8 +206,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   }
 }
 
-// Second pass: thread d of block (b, h) merges every split's partial of that (b, h). All of a
-// thread's partial loads are issued before the arithmetic (up to kMergeUnroll splits).
+// Second pass: thread d of block (b, h) merges every split's partial of that (b, h). When the
+// workspace holds at most kMergeUnroll splits, the loads of all of them are issued together with
+// the load of the sequence's length (indices clamped to the workspace, so no load waits on
+// another); splits past the length are then left out by selection, never by arithmetic, so
+// whatever an unwritten slot holds cannot reach the result.
 constexpr int kMergeUnroll = 16;
 
 template <typename T, int D>
@@ -215,33 +218,33 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
   const int bh = blockIdx.x;
   const int b = bh / p.Hq;
   const int d = threadIdx.x;
-  int len = p.lengths[b];
-  len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
-  const int nvalid = (len + p.split_len - 1) / p.split_len;
   const float* part = p.ws + (int64_t)bh * p.nsplit * (D + 2);
   float M = -INFINITY, L = 0.f, acc = 0.f;
-  if (nvalid <= kMergeUnroll) {
+  if (p.nsplit <= kMergeUnroll) {
     float m[kMergeUnroll], l[kMergeUnroll], o[kMergeUnroll];
+    const int last = p.nsplit - 1;
 #pragma unroll
     for (int s = 0; s < kMergeUnroll; ++s) {
-      if (s < nvalid) {
-        m[s] = part[s * (D + 2) + D];
-        l[s] = part[s * (D + 2) + D + 1];
-        o[s] = part[s * (D + 2) + d];
-      }
+      const float* ps = part + min(s, last) * (D + 2);
+      m[s] = ps[D];
+      l[s] = ps[D + 1];
+      o[s] = ps[d];
     }
+    int len = p.lengths[b];
+    len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+    const int nvalid = (len + p.split_len - 1) / p.split_len;
 #pragma unroll
-    for (int s = 0; s < kMergeUnroll; ++s)
-      if (s < nvalid) M = fmaxf(M, m[s]);
+    for (int s = 0; s < kMergeUnroll; ++s) M = s < nvalid ? fmaxf(M, m[s]) : M;
 #pragma unroll
     for (int s = 0; s < kMergeUnroll; ++s) {
-      if (s < nvalid) {
-        const float w = __builtin_amdgcn_exp2f(m[s] - M);
-        L = __builtin_fmaf(w, l[s], L);
-        acc = __builtin_fmaf(w, o[s], acc);
-      }
+      const float w = __builtin_amdgcn_exp2f(m[s] - M);
+      L = s < nvalid ? __builtin_fmaf(w, l[s], L) : L;
+      acc = s < nvalid ? __builtin_fmaf(w, o[s], acc) : acc;
     }
   } else {
+    int len = p.lengths[b];
+    len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+    const int nvalid = (len + p.split_len - 1) / p.split_len;
     for (int s = 0; s < nvalid; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
     for (int s = 0; s < nvalid; ++s) {
       const float w = __builtin_amdgcn_exp2f(part[s * (D + 2) + D] - M);
@@ -339,34 +342,41 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
   const __bf16* kb = static_cast<const __bf16*>(p.k) + slab + (int64_t)k0 * D;
   const __bf16* vb = static_cast<const __bf16*>(p.v) + slab + (int64_t)k0 * D;
 
-  // ---- issue every K and V load of the split up front. K: a lane quad owns a key row and
-  // each load instruction of the quad reads one contiguous 64-byte segment of it.
+  // ---- issue the query load, then every K and V load of the split, before any arithmetic.
+  // The loads are unconditional (no branch around a load, so the compiler inserts no wait
+  // between them): a row past the split's last valid key re-reads that last key, whose score
+  // is then replaced by -inf, so its probability is exactly 0. In that order the query is
+  // waited for first, K next and V last, so the scores start while V is still in flight.
+  const __bf16* qg = static_cast<const __bf16*>(p.q) + ((int64_t)b * p.Hq + (int64_t)g * p.G) * D;
+  static_assert(G * (D / 8) <= kFastThreads, "one 16-byte query chunk per thread");
+  const int qi = min(tid, G * (D / 8) - 1);
+  const u32x4 qraw = *reinterpret_cast<const u32x4*>(qg + (int64_t)(qi / (D / 8)) * D + (qi % (D / 8)) * 8);
+  // K: a lane quad owns a key row and each load instruction of the quad reads one contiguous
+  // 64-byte segment of it.
   const int kq = tid % 4;
   u32x4 kr[KP][KC];
 #pragma unroll
   for (int ps = 0; ps < KP; ++ps) {
-    const int row = ps * KROWS + tid / 4;
+    const int row = min(ps * KROWS + tid / 4, nk - 1);
 #pragma unroll
-    for (int cc = 0; cc < KC; ++cc) {
-      kr[ps][cc] = row < nk ? *reinterpret_cast<const u32x4*>(kb + (int64_t)row * D + (cc * 4 + kq) * 8)
-                            : u32x4{0, 0, 0, 0};
-    }
+    for (int cc = 0; cc < KC; ++cc)
+      kr[ps][cc] = *reinterpret_cast<const u32x4*>(kb + (int64_t)row * D + (cc * 4 + kq) * 8);
   }
   const int vc = tid % LPRV;
   const int vslot = tid / LPRV;
   u32x4 vr[VR];
 #pragma unroll
   for (int i = 0; i < VR; ++i) {
-    const int row = i * VS + vslot;
-    vr[i] = row < nk ? *reinterpret_cast<const u32x4*>(vb + (int64_t)row * D + vc * 8) : u32x4{0, 0, 0, 0};
+    const int row = min(i * VS + vslot, nk - 1);
+    vr[i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)row * D + vc * 8);
   }
 
+  // every load above is issued before the query's LDS store waits for its data
+  __builtin_amdgcn_sched_barrier(0);
   // ---- the group's query vectors into LDS
-  const __bf16* qg = static_cast<const __bf16*>(p.q) + ((int64_t)b * p.Hq + (int64_t)g * p.G) * D;
-  for (int idx = tid; idx < G * (D / 8); idx += kFastThreads) {
-    const int h = idx / (D / 8), c = idx % (D / 8);
-    *reinterpret_cast<u32x4*>(&s_q[h][c * 8]) = *reinterpret_cast<const u32x4*>(qg + (int64_t)h * D + c * 8);
-  }
+  // (threads past the last chunk store that chunk again: the same bytes to the same address; an
+  // unconditional store keeps the compiler from sinking the query load behind the K/V loads)
+  *reinterpret_cast<u32x4*>(&s_q[qi / (D / 8)][(qi % (D / 8)) * 8]) = qraw;
   __syncthreads();
 
   // ---- scores (log2 units): 4 lanes per key row, DPP sum inside each lane quad

@@ -206,37 +206,45 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   }
 }
 
-// Second pass: thread d of block (b, h) merges every split's partial of that (b, h). When the
-// workspace holds at most kMergeUnroll splits, the loads of all of them are issued together with
-// the load of the sequence's length (indices clamped to the workspace, so no load waits on
-// another); splits past the length are then left out by selection, never by arithmetic, so
-// whatever an unwritten slot holds cannot reach the result.
-constexpr int kMergeUnroll = 16;
-
-template <typename T, int D>
+// Second pass: thread d of block (b, h) merges every split's partial of that (b, h). NS is the
+// workspace's split count when it is small enough to unroll (0: a runtime loop). Unrolled, the
+// loads of every split's partial are issued together with the load of the sequence's length, so
+// no load waits on another; splits past the length are then left out by selection, never by
+// arithmetic, so whatever an unwritten slot holds cannot reach the result.
+template <typename T, int D, int NS>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
-  const int bh = blockIdx.x;
-  const int b = bh / p.Hq;
+  const int b = blockIdx.y;
+  const int bh = b * p.Hq + blockIdx.x;
   const int d = threadIdx.x;
   const float* part = p.ws + (int64_t)bh * p.nsplit * (D + 2);
   float M = -INFINITY, L = 0.f, acc = 0.f;
-  if (p.nsplit <= kMergeUnroll) {
-    float m[kMergeUnroll], l[kMergeUnroll], o[kMergeUnroll];
-    const int last = p.nsplit - 1;
+  if constexpr (NS > 0) {
+    static_assert(NS <= 64, "one lane per split");
+    // lane t of each wave loads split min(t, NS-1)'s (max, sum) pair; the pairs are broadcast
+    // from those lanes with v_readlane once they have arrived
+    const int lane = d % 64;
+    const float2 ml = *reinterpret_cast<const float2*>(part + min(lane, NS - 1) * (D + 2) + D);
+    float o[NS];
 #pragma unroll
-    for (int s = 0; s < kMergeUnroll; ++s) {
-      const float* ps = part + min(s, last) * (D + 2);
-      m[s] = ps[D];
-      l[s] = ps[D + 1];
-      o[s] = ps[d];
-    }
+    for (int s = 0; s < NS; ++s) o[s] = part[s * (D + 2) + d];
     int len = p.lengths[b];
+    // every load above is in flight before the first wait: the empty asm uses each loaded
+    // register, so no load can be sunk into a branch below it
+#pragma unroll
+    for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(o[s]));
+    asm volatile("" ::"v"(ml.x), "v"(ml.y), "s"(len));
     len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
     const int nvalid = (len + p.split_len - 1) / p.split_len;
+    float m[NS], l[NS];
 #pragma unroll
-    for (int s = 0; s < kMergeUnroll; ++s) M = s < nvalid ? fmaxf(M, m[s]) : M;
+    for (int s = 0; s < NS; ++s) {
+      m[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.x), s));
+      l[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.y), s));
+    }
 #pragma unroll
-    for (int s = 0; s < kMergeUnroll; ++s) {
+    for (int s = 0; s < NS; ++s) M = s < nvalid ? fmaxf(M, m[s]) : M;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
       const float w = __builtin_amdgcn_exp2f(m[s] - M);
       L = s < nvalid ? __builtin_fmaf(w, l[s], L) : L;
       acc = s < nvalid ? __builtin_fmaf(w, o[s], acc) : acc;
@@ -257,6 +265,36 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
   T* out = static_cast<T*>(p.o) + (int64_t)bh * D;
   out[d] = empty ? (T)0.f : (T)(acc / L);
   if (p.lse && d == 0) p.lse[bh] = empty ? -INFINITY : (M + __builtin_amdgcn_logf(L)) * kLn2;
+}
+
+template <typename T, int D, int NS>
+void launch_merge_ns(const DecParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, NS>), dim3(p.Hq, p.B), dim3(D), 0, stream, p);
+}
+
+// The merge pass for the workspace's split count: unrolled up to 16 splits (a 4096-key cache at
+// 256 keys per split), a runtime loop beyond.
+template <typename T, int D>
+void launch_merge(const DecParams& p, hipStream_t stream) {
+  switch (p.nsplit) {
+    case 1: launch_merge_ns<T, D, 1>(p, stream); break;
+    case 2: launch_merge_ns<T, D, 2>(p, stream); break;
+    case 3: launch_merge_ns<T, D, 3>(p, stream); break;
+    case 4: launch_merge_ns<T, D, 4>(p, stream); break;
+    case 5: launch_merge_ns<T, D, 5>(p, stream); break;
+    case 6: launch_merge_ns<T, D, 6>(p, stream); break;
+    case 7: launch_merge_ns<T, D, 7>(p, stream); break;
+    case 8: launch_merge_ns<T, D, 8>(p, stream); break;
+    case 9: launch_merge_ns<T, D, 9>(p, stream); break;
+    case 10: launch_merge_ns<T, D, 10>(p, stream); break;
+    case 11: launch_merge_ns<T, D, 11>(p, stream); break;
+    case 12: launch_merge_ns<T, D, 12>(p, stream); break;
+    case 13: launch_merge_ns<T, D, 13>(p, stream); break;
+    case 14: launch_merge_ns<T, D, 14>(p, stream); break;
+    case 15: launch_merge_ns<T, D, 15>(p, stream); break;
+    case 16: launch_merge_ns<T, D, 16>(p, stream); break;
+    default: launch_merge_ns<T, D, 0>(p, stream); break;
+  }
 }
 
 // Merge of decode results computed over disjoint slices of every sequence's keys (the shards of
@@ -531,17 +569,17 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   if (p.B == 0 || p.Hq == 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
     if (a.d == 128 && launch_fast_128(p, stream)) {
-      hipLaunchKernelGGL((decode_merge_kernel<T, 128>), dim3(p.B * p.Hq), dim3(128), 0, stream, p);
+      launch_merge<T, 128>(p, stream);
       return hipGetLastError();
     }
   }
   dim3 g1(p.nsplit, p.Hkv, p.B);
   if (a.d == 128) {
     hipLaunchKernelGGL((decode_split_kernel<T, 128>), g1, dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL((decode_merge_kernel<T, 128>), dim3(p.B * p.Hq), dim3(128), 0, stream, p);
+    launch_merge<T, 128>(p, stream);
   } else if (a.d == 64) {
     hipLaunchKernelGGL((decode_split_kernel<T, 64>), g1, dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL((decode_merge_kernel<T, 64>), dim3(p.B * p.Hq), dim3(64), 0, stream, p);
+    launch_merge<T, 64>(p, stream);
   } else {
     return hipErrorInvalidValue;
   }
@@ -566,17 +604,16 @@ hipError_t launch_decode_split_merge(const int32_t* lengths, float* ws, void* o,
   p.max_len = max_len;
   p.nsplit = decode_nsplit(max_len);
   p.split_len = kDecodeSplitLen;
-  const dim3 grid((unsigned)((int64_t)batch * hq));
   if (d == 128) {
     if (bf16)
-      hipLaunchKernelGGL((decode_merge_kernel<__bf16, 128>), grid, dim3(128), 0, stream, p);
+      launch_merge<__bf16, 128>(p, stream);
     else
-      hipLaunchKernelGGL((decode_merge_kernel<float, 128>), grid, dim3(128), 0, stream, p);
+      launch_merge<float, 128>(p, stream);
   } else if (d == 64) {
     if (bf16)
-      hipLaunchKernelGGL((decode_merge_kernel<__bf16, 64>), grid, dim3(64), 0, stream, p);
+      launch_merge<__bf16, 64>(p, stream);
     else
-      hipLaunchKernelGGL((decode_merge_kernel<float, 64>), grid, dim3(64), 0, stream, p);
+      launch_merge<float, 64>(p, stream);
   } else {
     return hipErrorInvalidValue;
   }

@@ -94,6 +94,20 @@ __global__ __launch_bounds__(kI8Threads) void decode_i8_split_kernel(I8Params p)
   const int8_t* kt = p.k + row0 * D;
   const char* vt = reinterpret_cast<const char*>(p.v + row0 * D);
 
+  // Every load of the split is issued before the first wait, V first. The V copies go straight
+  // to LDS through inline asm, which the compiler does not count: issued ahead of every load it
+  // does count, and with loads returning in order, each wait the compiler places for its own
+  // loads also covers them. No load sits in a branch (a branch around a load lets the compiler
+  // place a wait inside it).
+  // ---- V rows of this wave into LDS: copy u moves rows 64 wave + 8u .. + 7 (1 KB); lane l
+  // fills slot l & 7 of row l >> 3 with the chunk that the swizzle puts there.
+  const unsigned lds_v = (unsigned)(uintptr_t)s_v;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int r = wave * 64 + u * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    dma16_sv(vt, (unsigned)(min(r, nk - 1) * D + c * 16), lds_v + (wave * 64 + u * 8) * D);
+  }
   // ---- K: key block kb of this wave, row col, bytes [32 gq, 32 gq + 32). Rows past the valid
   // length re-read the last valid row (finite; their scores are masked).
   u32x4 kr[4][2];
@@ -104,31 +118,25 @@ __global__ __launch_bounds__(kI8Threads) void decode_i8_split_kernel(I8Params p)
     kr[kb][0] = src[0];
     kr[kb][1] = src[1];
   }
-  // ---- queries (B operand): head col of the block, dims 32 gq + 8 i .. + 7 for k-step i
+  // ---- queries (B operand): head col of the block, dims 32 gq + 8 i .. + 7 for k-step i. A
+  // column past the group's last head reads that head and is then zeroed.
   const int hg = hb * kHeadBlock + col;  // head within the group
+  const bool hvalid = hg < p.G;
   bf16x8 qf[4];
-  if (hg < p.G) {
-    const __bf16* qh = p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G + hg) * D + 32 * gq;
+  {
+    const __bf16* qh = p.q + ((int64_t)b * p.Hq + (int64_t)g * p.G + min(hg, p.G - 1)) * D + 32 * gq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qf[i] = *reinterpret_cast<const bf16x8*>(qh + 8 * i);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qf[i] = bf16x8{};
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(qh + 8 * i);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qf[i] = __builtin_bit_cast(bf16x8, hvalid ? raw : z);
+    }
   }
   // ---- row scales of the split
   {
     const int row = min(tid, nk - 1);
     s_ks[tid] = p.ks[row0 + row];
     s_vs[tid] = p.vs[row0 + row];
-  }
-  // ---- V rows of this wave into LDS: copy u moves rows 64 wave + 8u .. + 7 (1 KB); lane l
-  // fills slot l & 7 of row l >> 3 with the chunk that the swizzle puts there.
-  const unsigned lds_v = (unsigned)(uintptr_t)s_v;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int r = wave * 64 + u * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    dma16_sv(vt, (unsigned)(min(r, nk - 1) * D + c * 16), lds_v + (wave * 64 + u * 8) * D);
   }
   __syncthreads();  // row scales visible
 

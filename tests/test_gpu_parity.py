@@ -299,6 +299,57 @@ def test_permute_full_size_llama70b():
     assert torch.equal(out[:, pos.to(DEV)].cpu(), pf.q[:, pos])
 
 
+@pytest.mark.parametrize("w", [synth.LLAMA31_70B_S131K, synth.DEEPSEEK_V3_MLA_S32K], ids=lambda w: w.name)
+def test_attention_full_size_identical_keys_every_row(w):
+    """Every row and head of every rank at full size, against a closed form. All keys of a kv
+    head are set equal (k_j = k_g, the natural-order row 0), so every visible key gets the same
+    weight: O_i is the mean of v_j over the keys with position <= the row's position (a prefix
+    mean of V in natural order), and LSE_i = scale * q_i . k_g + ln(pos_i + 1).
+
+    The kernel's probabilities are then exactly 1 and its row sum is the exact count of visible
+    keys, so the comparison can be tight: O within bf16 rounding (2^-8 |O| + 1e-5), and LSE within
+    2e-5 once the expected logit models the kernel's one documented rounding of the scores' input
+    (the query times scale * log2(e) in float32, rounded to bfloat16, then an exact product with
+    k_g); what is left is float32 accumulation (observed at most 2.8e-6). A visible-key count off
+    by 2e-5 of itself (3 keys at position 131071, 1 key below position 50000) fails the LSE check
+    in any row; a wrong row, head or kv group fails both."""
+    pf = full_workload(w)
+    cp = w.cps[-1]
+    S, c = w.seq, w.seq // (2 * cp)
+    G = w.hq // w.hkv
+    k1d = pf.kd[:, :1].expand(-1, S, -1, -1).contiguous()
+    kp = cpa.permute(k1d, cp)
+    vp = pf.kv_perm(cp)[1]
+    k1 = pf.k[0, 0].double()                                                   # [Hkv, Dqk]
+    sl2 = torch.tensor(pf.scale, dtype=torch.float32) * torch.tensor(math.log2(math.e), dtype=torch.float32)
+    worst_o = worst_l = 0.0
+    for r in range(cp):
+        announce(f"{w.name} identical keys, every row: cp={cp} rank={r}")
+        qs = cpa.permute(pf.qd, cp, row_begin=r * 2 * c, row_count=2 * c)
+        o, lse = cpa.attention_fwd(qs, kp, vp, cp, r, scale=pf.scale)
+        torch.cuda.synchronize()
+        o, lse = o[0].float().cpu(), lse[0].cpu().double()                    # [Sq, Hq, Dv], [Hq, Sq]
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+        pos = torch.from_numpy(olb.shard_positions(S, cp, r)).long()
+        cnt = (pos + 1).double()
+        for g in range(w.hkv):
+            hs = slice(g * G, (g + 1) * G)
+            pref = pf.v[0, :, g].double().cumsum(0)[pos] / cnt[:, None]      # [Sq, Dv]
+            err_o = (o[:, hs].double() - pref[:, None, :]).abs()
+            tol_o = pref.abs()[:, None, :] * 2.0 ** -8 + 1e-5
+            bad = err_o > tol_o
+            assert not bad.any(), (f"O rank {r} group {g}: {int(bad.sum())} elements beyond bf16 rounding, "
+                                   f"max err {float(err_o.max()):.3e}")
+            qr = (pf.q[0, pos, hs].float() * sl2).to(torch.bfloat16).double()  # [Sq, G, Dqk]
+            lse_ref = (qr @ k1[g]) * math.log(2.0) + torch.log(cnt)[:, None]  # [Sq, G]
+            err_l = (lse[hs].T - lse_ref).abs()
+            assert float(err_l.max()) <= 2e-5, f"LSE rank {r} group {g}: max err {float(err_l.max()):.3e}"
+            worst_o = max(worst_o, float((err_o / tol_o).max()))
+            worst_l = max(worst_l, float(err_l.max()))
+    print(f"  every row of every rank: O error at most {worst_o:.3f} of its bf16 bound, LSE error at most "
+          f"{worst_l:.2e}", flush=True)
+
+
 def test_tiny_workload_full():
     w = synth.TINY_CP2_F32
     pf = Prefill(w.batch, w.seq, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype, w.seed)

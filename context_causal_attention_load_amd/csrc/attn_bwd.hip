@@ -426,11 +426,14 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
 #pragma unroll
   for (int m = 0; m < C::MV; ++m) dvacc[m] = f32x16{};
 
-  // stages: (query block qb, head h of the group); blocks whose rows all precede the keys skip
+  // stages: (query block qb, head h of the group), from the shard's last block down; blocks
+  // whose rows all precede the keys skip. Streaming from the end puts every workgroup of a kv
+  // head at the same rows when it starts (each row block is seen by all keys before it), so the
+  // workgroups of an XCD read the same stages at about the same time and share its L2.
   const int* blkmin = e.blk;
   const int* blkmax = e.blk + e.nqb;
-  auto next_visible = [&](int qb) {
-    while (qb < e.nqb && load_uniform_i32(blkmax + qb) < kpos0) ++qb;
+  auto prev_visible = [&](int qb) {
+    while (qb >= 0 && load_uniform_i32(blkmax + qb) < kpos0) --qb;
     return qb;
   };
 
@@ -487,19 +490,19 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
   const int tr_q = lane % 4;
   const int kpos = kpos0 + kk;
 
-  // stage sequence: (query block, head of the group), heads fastest; qb == nqb marks the end
+  // stage sequence: (query block, head of the group), heads fastest; qb < 0 marks the end
   auto advance = [&](int& sqb, int& sh) {
-    if (sqb >= e.nqb) return;
+    if (sqb < 0) return;
     if (++sh == p.G) {
       sh = 0;
-      sqb = next_visible(sqb + 1);
+      sqb = prev_visible(sqb - 1);
     }
   };
-  int qb = next_visible(0), h = 0;
+  int qb = prev_visible(e.nqb - 1), h = 0;
   int qb1 = qb, h1 = h;
   advance(qb1, h1);
-  if (qb < e.nqb) dma_stage(qb, g * p.G + h, 0);
-  if (qb1 < e.nqb) {
+  if (qb >= 0) dma_stage(qb, g * p.G + h, 0);
+  if (qb1 >= 0) {
     dma_stage(qb1, g * p.G + h1, 1);
     wait_all_but_one_stage();
   } else {
@@ -507,11 +510,11 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
   }
   __syncthreads();
   int buf = 0;
-  while (qb < e.nqb) {
+  while (qb >= 0) {
     int qb2 = qb1, h2 = h1;
     advance(qb2, h2);
     const int buf2 = buf >= kKvStages - 2 ? buf + 2 - kKvStages : buf + 2;
-    if (qb2 < e.nqb) dma_stage(qb2, g * p.G + h2, buf2);  // that slot was last read two stages ago
+    if (qb2 >= 0) dma_stage(qb2, g * p.G + h2, buf2);  // that slot was last read two stages ago
 
     const char* qt = lds + buf * C::STAGE;
     const char* ot = qt + C::Q_BYTES;
@@ -635,7 +638,7 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
     // the next stage's copies must have landed; the one after may stay in flight
-    if (qb2 < e.nqb)
+    if (qb2 >= 0)
       wait_all_but_one_stage();
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -17,8 +17,10 @@ removes (`load_balance`; skip with --no-balance-demo); and every rank's backward
 
 Also measured: GQA decode (Mixtral-8x22B shape, batch 24, 48/8 heads, D 128, cache 2048 with
 lengths uniform in [1024, 2048]), rotating 4 cache copies so reads come from HBM rather than
-the 256 MB last-level cache; the same decode over an int8-quantized cache (6 copies); and the CPU fp64 oracle on a bounded row sample of the same
-prefill workload (the CPU baseline).
+the 256 MB last-level cache; the same decode over an int8-quantized cache (6 copies); every
+rank's attention kernel at the other prefill shapes (`other_configs`: Llama2-7B MHA at 8192
+tokens, cp 1 and 4; DeepSeek-V3 MLA at 32768 tokens, cp 4; skip with --no-other-configs); and
+the CPU fp64 oracle on a bounded row sample of the same prefill workload (the CPU baseline).
 
 Prints one JSON line.
 """
@@ -228,6 +230,45 @@ def _time_calls(call, iters):
     return ms, t0.elapsed_time(t1) / iters
 
 
+def other_configs_ms(dev, iters=5):
+    """Every rank's attention kernel at the other prefill shapes (the 8192-token Llama2-7B MHA at
+    cp = 1 and cp = 4, the 32768-token DeepSeek-V3 MLA shape at cp = 4): HIP-event time of one
+    launch after a warm-up, median of ``iters``. Inputs are seeded N(0,1) draws on the device
+    (timing only; these shapes' parity is in the tests)."""
+    import context_causal_attention_load_amd as cpa
+    from context_causal_attention_load_amd import synth
+
+    out = []
+    for w in (synth.LLAMA2_7B_S8K, synth.DEEPSEEK_V3_MLA_S32K):
+        gen = torch.Generator(device=dev).manual_seed(w.seed)
+        qd, kd, vd = (torch.randn((w.batch, w.seq, h, d), generator=gen, device=dev, dtype=torch.float32).to(w.dtype)
+                      for h, d in ((w.hq, w.d_qk), (w.hkv, w.d_qk), (w.hkv, w.d_v)))
+        for cp in w.cps:
+            c = w.seq // (2 * cp)
+            kp, vp = cpa.permute(kd, cp), cpa.permute(vd, cp)
+            o = torch.empty((w.batch, 2 * c, w.hq, w.d_v), dtype=w.dtype, device=dev)
+            lse = torch.empty((w.batch, w.hq, 2 * c), dtype=torch.float32, device=dev)
+            ms = []
+            for r in range(cp):
+                qs = cpa.permute(qd, cp, row_begin=r * 2 * c, row_count=2 * c)
+                cpa.attention_fwd(qs, kp, vp, cp, r, scale=w.scale, out=o, lse=lse)
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+                for a, b in evs:
+                    a.record()
+                    cpa.attention_fwd(qs, kp, vp, cp, r, scale=w.scale, out=o, lse=lse)
+                    b.record()
+                torch.cuda.synchronize()
+                ms.append(sorted(a.elapsed_time(b) for a, b in evs)[iters // 2])
+            flops = useful_flops(w.seq, cp, w.hq, w.d_qk, w.d_v, w.batch)
+            avg = sum(ms) / len(ms)
+            tf = flops / (avg * 1e-3) / 1e12
+            out.append({"workload": f"{w.name} cp={cp}", "ms_per_rank": [round(x, 3) for x in ms],
+                        "useful_flop_per_rank": flops, "tflops": round(tf, 1),
+                        "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        del qd, kd, vd
+    return out
+
+
 def bench_decode(w, iters, dev, copies=4):
     import context_causal_attention_load_amd as cpa
     from context_causal_attention_load_amd import synth
@@ -330,6 +371,8 @@ def main():
                     help="skip the backward-pass timing (after the timed forward steps)")
     ap.add_argument("--no-balance-demo", action="store_true",
                     help="skip the per-rank balanced vs contiguous shard timing (after the timed steps)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the per-rank attention timing at the other prefill shapes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share (one context-parallel rank); runs on more than one GPU "
@@ -417,6 +460,8 @@ def main():
                          "traffic": profiled_traffic("decode_int8_mixtral8x22b_b24_l2048.md",
                                                      ("decode_int8.hip", "decode.hip", "common.h")),
                          "traffic_unit": "HBM bytes per call (split + merge)", "algorithmic_bytes": d8["bytes"]}}
+    if not args.no_other_configs:
+        result["other_configs"] = other_configs_ms(dev)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, cp, 0, args.cpu_rows)
         cb.pop("seconds")

@@ -210,6 +210,23 @@ def balance_demo_ms(w, cp, qd, kd, vd, kp, vp, q_shard, o_shard, lse_shard):
             "contiguous_max_over_mean_closed_form": round((2 * cp - 1) / cp, 4)}
 
 
+def decode_bytes(w, lengths, elt=2):
+    """Algorithmic HBM bytes of one decode call: the valid K and V rows of every sequence and kv
+    head (elt bytes per element), q read and o written, the fp32 LSE written, the int32 lengths."""
+    kv_bytes = int(lengths.sum()) * w.hkv * w.d * elt * 2
+    io_bytes = w.batch * w.hq * w.d * elt * 2 + w.batch * w.hq * 4 + w.batch * 4
+    return kv_bytes + io_bytes
+
+
+def decode_int8_bytes(w, lengths):
+    """The same over an int8 cache: one byte per K and V code plus a float32 scale per valid row
+    of K and of V; q and o stay bf16."""
+    rows = int(lengths.sum()) * w.hkv
+    kv_bytes = rows * w.d * 2 + rows * 4 * 2
+    io_bytes = w.batch * w.hq * w.d * 2 * 2 + w.batch * w.hq * 4 + w.batch * 4
+    return kv_bytes + io_bytes
+
+
 def _time_calls(call, iters):
     """Times ``call(i)`` two ways on the current stream: each call between its own pair of HIP
     events (sorted per-call milliseconds), and ``iters`` calls back to back between one pair
@@ -284,15 +301,13 @@ def bench_decode(w, iters, dev, copies=4):
     for i in range(copies):
         cpa.decode(qd, caches[i][0], caches[i][1], ld, scale=w.scale, workspace=ws, out=out, lse=lse)
     torch.cuda.synchronize()
+
     def call(i):
         kci, vci = caches[i % copies]
         cpa.decode(qd, kci, vci, ld, scale=w.scale, workspace=ws, out=out, lse=lse)
 
     ms, b2b = _time_calls(call, iters)
-    elt = 2
-    kv_bytes = int(lengths.sum()) * w.hkv * w.d * elt * 2
-    io_bytes = w.batch * w.hq * w.d * elt * 2 + w.batch * w.hq * 4 + w.batch * 4
-    alg = kv_bytes + io_bytes
+    alg = decode_bytes(w, lengths)
     med = ms[len(ms) // 2]
     return dict(median_ms=med, min_ms=ms[0], b2b_ms=b2b, bytes=alg, gbs=alg / (med * 1e-3) / 1e9,
                 b2b_gbs=alg / (b2b * 1e-3) / 1e9)
@@ -315,15 +330,13 @@ def bench_decode_int8(w, iters, dev, copies=6):
     for c in caches:
         cpa.decode_int8(qd, c[0], c[1], c[2], c[3], ld, scale=w.scale, workspace=ws, out=out, lse=lse)
     torch.cuda.synchronize()
+
     def call(i):
         c = caches[i % copies]
         cpa.decode_int8(qd, c[0], c[1], c[2], c[3], ld, scale=w.scale, workspace=ws, out=out, lse=lse)
 
     ms, b2b = _time_calls(call, iters)
-    rows = int(lengths.sum()) * w.hkv
-    kv_bytes = rows * w.d * 2 + rows * 4 * 2          # K and V codes, K and V row scales
-    io_bytes = w.batch * w.hq * w.d * 2 * 2 + w.batch * w.hq * 4 + w.batch * 4
-    alg = kv_bytes + io_bytes
+    alg = decode_int8_bytes(w, lengths)
     med = ms[len(ms) // 2]
     return dict(median_ms=med, min_ms=ms[0], b2b_ms=b2b, bytes=alg, gbs=alg / (med * 1e-3) / 1e9,
                 b2b_gbs=alg / (b2b * 1e-3) / 1e9)

@@ -101,6 +101,13 @@ def _need_gpu(*tensors):
             raise ValueError("tensors must be contiguous (no implicit copies are made)")
 
 
+def _check_buf(t, shape, dtype, name):
+    """A caller-provided output must have exactly the shape and dtype the call writes: the
+    library receives a raw pointer and cannot see how large the buffer is."""
+    if t is not None and (tuple(t.shape) != tuple(shape) or t.dtype != dtype):
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
 # ---------------------------------------------------------------------------- index helpers
 
 def lb_source_index(seq, cp, j):
@@ -185,6 +192,8 @@ def attention_fwd(q_shard, k, v, cp, rank, q_positions=None, scale=None, out=Non
         raise ValueError("q_positions must be int32 [Sq]")
     if scale is None:
         scale = 1.0 / math.sqrt(Dqk)
+    _check_buf(out, (B, Sq, Hq, Dv), q_shard.dtype, "out")
+    _check_buf(lse, (B, Hq, Sq), torch.float32, "lse")
     if out is None:
         out = torch.empty((B, Sq, Hq, Dv), dtype=q_shard.dtype, device=q_shard.device)
     if lse is None and want_lse:
@@ -217,6 +226,8 @@ def decode(q, k_cache, v_cache, lengths, scale=None, workspace=None, out=None, l
     need = decode_workspace_bytes(B, Hq, Hkv, Lmax, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_buf(out, (B, Hq, D), q.dtype, "out")
+    _check_buf(lse, (B, Hq), torch.float32, "lse")
     if out is None:
         out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
     if lse is None and want_lse:
@@ -239,6 +250,8 @@ def decode_merge(o_parts, lse_parts, out=None, lse=None, want_lse=True):
     R, B, Hq, D = o_parts.shape
     if lse_parts.dtype != torch.float32 or tuple(lse_parts.shape) != (R, B, Hq):
         raise ValueError("lse_parts must be float32 [R, B, Hq]")
+    _check_buf(out, (B, Hq, D), o_parts.dtype, "out")
+    _check_buf(lse, (B, Hq), torch.float32, "lse")
     if out is None:
         out = torch.empty((B, Hq, D), dtype=o_parts.dtype, device=o_parts.device)
     if lse is None and want_lse:
@@ -296,6 +309,8 @@ def decode_int8(q, k_codes, k_scales, v_codes, v_scales, lengths, scale=None, wo
     need = decode_workspace_bytes(B, Hq, Hkv, Lmax, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_buf(out, (B, Hq, D), q.dtype, "out")
+    _check_buf(lse, (B, Hq), torch.float32, "lse")
     if out is None:
         out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
     if lse is None and want_lse:
@@ -338,6 +353,9 @@ def attention_bwd(q_shard, k, v, o, lse, d_o, cp, rank, q_positions=None, scale=
     dev = q_shard.device
     if workspace is None:
         workspace = torch.empty(max(attention_bwd_workspace_bytes(B, Sq, Hq), 16), dtype=torch.uint8, device=dev)
+    _check_buf(dq, (B, Sq, Hq, Dqk), torch.float32, "dq")
+    _check_buf(dk, (B, S, Hkv, Dqk), torch.float32, "dk")
+    _check_buf(dv, (B, S, Hkv, Dv), torch.float32, "dv")
     if dq is None:
         dq = torch.empty((B, Sq, Hq, Dqk), dtype=torch.float32, device=dev)
     if dk is None:

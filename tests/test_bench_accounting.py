@@ -60,3 +60,18 @@ def test_profiled_traffic_only_while_sources_match(tmp_path, monkeypatch):
     (csrc / "k.hip").write_bytes(b"kernel source, changed\n")
     assert bench.profiled_traffic("p.md", ("k.hip",)) is None
     assert bench.profiled_traffic("missing.md", ("k.hip",)) is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """This build measures one GPU's share; a request for several GPUs ends with a message and a
+    non-zero status before anything runs."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""

@@ -374,8 +374,8 @@ def cpu_baseline(w, cp, rank, n_rows, seed=0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=16)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=24)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-iters", type=int, default=50)
     ap.add_argument("--cpu-rows", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -429,6 +429,8 @@ def main():
                                                  ("attn_fwd.hip", "attn_tiles.h", "common.h")),
                      "traffic_unit": "HBM bytes per launch",
                      "kernel": "attn_fwd_bf16_kernel<128,128>", "kernel_avg_ms": round(attn_avg_ms, 4),
+                     "kernel_median_ms": round(sorted(pre["attn_ms"])[len(pre["attn_ms"]) // 2], 4),
+                     "kernel_min_ms": round(min(pre["attn_ms"]), 4),
                      "useful_flop_per_launch": pre["flops"]},
         "per_rank_step_ms": {str(r): round(t, 3) for r, t in pre["per_rank_ms"].items()},
     }

@@ -52,6 +52,24 @@ __device__ __forceinline__ void dma16_sv(const char* base, unsigned voff, unsign
 // has its own L2.
 constexpr int kNumXcd = 8;
 
+// Decode work placement: a 1-D grid of decode_xcd_blocks(n_inner, hkv, batch) workgroups in
+// which block id -> (inner index, kv head g, sequence b) puts every block of kv head g on XCD
+// g % kNumXcd (id % kNumXcd). The split kernels use it with inner = split and the merge with
+// inner = query head within the group, so a kv head's partials are written and read on one XCD.
+// Blocks past the last kv head (when hkv is not a multiple of kNumXcd) return false.
+inline int64_t decode_xcd_blocks(int n_inner, int hkv, int batch) {
+  return (int64_t)kNumXcd * n_inner * ((hkv + kNumXcd - 1) / kNumXcd) * batch;
+}
+__device__ __forceinline__ bool decode_xcd_item(int id, int n_inner, int hkv, int batch, int& inner, int& g, int& b) {
+  const int xcd = id % kNumXcd, j = id / kNumXcd;  // j enumerates (sequence, kv head / kNumXcd, inner)
+  inner = j % n_inner;
+  const int t = j / n_inner;
+  const int ng = (hkv + kNumXcd - 1) / kNumXcd;
+  b = t / ng;
+  g = (t % ng) * kNumXcd + xcd;
+  return g < hkv && b < batch;
+}
+
 // ---- launchers (defined in the .hip files; return the launch status) ----
 hipError_t launch_permute(const void* src, void* dst, int64_t outer, int64_t seq, int64_t row_bytes,
                           int64_t cp, int64_t row_begin, int64_t row_count, bool scatter,
@@ -130,7 +148,7 @@ hipError_t launch_kv_quantize(const void* x, int8_t* codes, float* scales, int64
                               hipStream_t stream);
 // Second decode pass alone: merges the split partials in ws into o (bf16 or fp32) and lse.
 hipError_t launch_decode_split_merge(const int32_t* lengths, float* ws, void* o, float* lse, int batch, int hq,
-                                     int max_len, int d, bool bf16, hipStream_t stream);
+                                     int hkv, int max_len, int d, bool bf16, hipStream_t stream);
 
 // Decode split geometry, shared by the workspace-size query and the launcher. The workspace
 // holds the split partials [batch, hq, nsplit, d + 2] in float32: d unnormalised outputs, then

@@ -206,6 +206,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   }
 }
 
+// Block -> (sequence b, query head h) of the merge, with the kv head of h on the XCD where the
+// split kernel ran that kv head's splits (decode_xcd_item), so the partials may still be in
+// that XCD's L2.
+__device__ __forceinline__ bool merge_item(const DecParams& p, int& b, int& h) {
+  int hg, g;
+  if (!decode_xcd_item(blockIdx.x, p.G, p.Hkv, p.B, hg, g, b)) return false;
+  h = g * p.G + hg;
+  return true;
+}
+
 // Second pass: thread d of block (b, h) merges every split's partial of that (b, h). NS is the
 // workspace's split count when it is small enough to unroll (0: a runtime loop). Unrolled, the
 // loads of every split's partial are issued together with the load of the sequence's length, so
@@ -213,8 +223,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
 // arithmetic, so whatever an unwritten slot holds cannot reach the result.
 template <typename T, int D, int NS>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
-  const int b = blockIdx.y;
-  const int bh = b * p.Hq + blockIdx.x;
+  int b, h;
+  if (!merge_item(p, b, h)) return;
+  const int bh = b * p.Hq + h;
   const int d = threadIdx.x;
   const float* part = p.ws + (int64_t)bh * p.nsplit * (D + 2);
   float M = -INFINITY, L = 0.f, acc = 0.f;
@@ -269,7 +280,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
 
 template <typename T, int D, int NS>
 void launch_merge_ns(const DecParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_merge_kernel<T, D, NS>), dim3(p.Hq, p.B), dim3(D), 0, stream, p);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, NS>), dim3(decode_xcd_blocks(p.G, p.Hkv, p.B)), dim3(D), 0, stream, p);
 }
 
 // The merge pass for the workspace's split count: unrolled up to 16 splits (a 4096-key cache at
@@ -368,7 +379,8 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
   __shared__ float s_red[kFastWaves][G][D];
   __shared__ float s_m[G], s_l[G];
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int split, g, b;
+  if (!decode_xcd_item(blockIdx.x, p.nsplit, p.Hkv, p.B, split, g, b)) return;
   int len = p.lengths[b];
   len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
   const int k0 = split * SL;
@@ -530,8 +542,8 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
 
 template <int D, int G>
 void launch_fast(const DecParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_bf16_split_kernel<D, G>), dim3(p.nsplit, p.Hkv, p.B), dim3(kFastThreads), 0, stream,
-                     p);
+  hipLaunchKernelGGL((decode_bf16_split_kernel<D, G>), dim3(decode_xcd_blocks(p.nsplit, p.Hkv, p.B)),
+                     dim3(kFastThreads), 0, stream, p);
 }
 
 bool launch_fast_128(const DecParams& p, hipStream_t stream) {
@@ -592,8 +604,9 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) { return launch_typed<float>(a, stream); }
 
 hipError_t launch_decode_split_merge(const int32_t* lengths, float* ws, void* o, float* lse, int batch, int hq,
-                                     int max_len, int d, bool bf16, hipStream_t stream) {
+                                     int hkv, int max_len, int d, bool bf16, hipStream_t stream) {
   if (batch == 0 || hq == 0) return hipSuccess;
+  if (hkv <= 0 || hq % hkv != 0) return hipErrorInvalidValue;
   DecParams p{};
   p.lengths = lengths;
   p.ws = ws;
@@ -601,6 +614,8 @@ hipError_t launch_decode_split_merge(const int32_t* lengths, float* ws, void* o,
   p.lse = lse;
   p.B = batch;
   p.Hq = hq;
+  p.Hkv = hkv;
+  p.G = hq / hkv;
   p.max_len = max_len;
   p.nsplit = decode_nsplit(max_len);
   p.split_len = kDecodeSplitLen;

@@ -79,8 +79,9 @@ __global__ __launch_bounds__(kI8Threads) void decode_i8_split_kernel(I8Params p)
   __shared__ float s_max[kI8Waves][kHeadBlock];
   __shared__ float s_sum[kI8Waves][kHeadBlock];
 
-  const int split = blockIdx.x, b = blockIdx.z;
-  const int g = blockIdx.y / p.nhb, hb = blockIdx.y % p.nhb;
+  int inner, g, b;  // kv head g on XCD g % kNumXcd, as in the merge that reads the partials
+  if (!decode_xcd_item(blockIdx.x, p.nsplit * p.nhb, p.Hkv, p.B, inner, g, b)) return;
+  const int split = inner % p.nsplit, hb = inner / p.nsplit;
   int len = p.lengths[b];
   len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
   const int k0 = split * SL;
@@ -280,10 +281,11 @@ hipError_t launch_decode_int8(const DecodeInt8Args& a, hipStream_t stream) {
   p.max_len = a.max_len;
   p.nsplit = decode_nsplit(a.max_len);
   p.scale_log2 = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(decode_i8_split_kernel, dim3(p.nsplit, p.Hkv * p.nhb, p.B), dim3(kI8Threads), 0, stream, p);
+  hipLaunchKernelGGL(decode_i8_split_kernel, dim3(decode_xcd_blocks(p.nsplit * p.nhb, p.Hkv, p.B)), dim3(kI8Threads), 0,
+                     stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_decode_split_merge(a.lengths, a.ws, a.o, a.lse, a.batch, a.hq, a.max_len, kI8D, true, stream);
+  return launch_decode_split_merge(a.lengths, a.ws, a.o, a.lse, a.batch, a.hq, a.hkv, a.max_len, kI8D, true, stream);
 }
 
 hipError_t launch_kv_quantize(const void* x, int8_t* codes, float* scales, int64_t rows, int d, bool bf16,

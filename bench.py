@@ -376,7 +376,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=24)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--decode-iters", type=int, default=50)
+    ap.add_argument("--decode-iters", type=int, default=200)
     ap.add_argument("--cpu-rows", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")

@@ -388,8 +388,8 @@ def main():
                     help="skip the per-rank attention timing at the other prefill shapes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share (one context-parallel rank); runs on more than one GPU "
-              "are not part of this build", file=sys.stderr)
+        print("bench.py measures one GPU's share (one context-parallel rank) and does not run on more than "
+              "one GPU", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -63,7 +63,7 @@ def test_profiled_traffic_only_while_sources_match(tmp_path, monkeypatch):
 
 
 def test_bench_refuses_more_than_one_gpu():
-    """This build measures one GPU's share; a request for several GPUs ends with a message and a
+    """bench.py measures one GPU's share; a request for several GPUs ends with a message and a
     non-zero status before anything runs."""
     import os
     import subprocess

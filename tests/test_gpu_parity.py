@@ -384,6 +384,9 @@ def test_decode_full_workload_with_poisoned_tail():
     (2, 8, 8, 64, 513, torch.float32, [513, 17]),
     (5, 12, 4, 64, 1000, torch.bfloat16, [999, 1000, 512, 3, 768]),
     (2, 4, 2, 128, 64, torch.float32, [64, 33]),
+    # 12 kv heads: workgroups are placed by kv head on 8 XCDs, so heads 8..11 form a second group
+    (2, 24, 12, 128, 700, torch.bfloat16, [700, 300]),
+    (2, 36, 12, 64, 200, torch.float32, [200, 1]),
 ])
 def test_decode_edge_lengths(batch, hq, hkv, d, max_len, dtype, lens):
     announce(f"decode B={batch} Hq={hq} Hkv={hkv} D={d} Lmax={max_len} {dtype} lens={lens}")
@@ -522,6 +525,7 @@ def test_decode_int8_full_workload_with_poisoned_tail():
     (2, 64, 2, 130, [64, 130]),              # G = 32
     (5, 12, 4, 1000, [999, 1000, 512, 3, 768]),
     (2, 1, 1, 1, [1, 1]),                    # one key, one head
+    (2, 36, 12, 600, [600, 129]),            # 12 kv heads: a second group of kv heads per XCD
 ])
 def test_decode_int8_edge_lengths(batch, hq, hkv, max_len, lens):
     announce(f"int8 decode B={batch} Hq={hq} Hkv={hkv} Lmax={max_len} lens={lens}")

@@ -698,3 +698,50 @@ def test_backward_deepseek_mla_full_size_sampled(rank):
 @pytest.mark.parametrize("rank", [0, 7])
 def test_backward_llama70b_full_size_sampled(rank):
     sampled_bwd_check(synth.LLAMA31_70B_S131K, 8, rank)
+
+
+def test_backward_llama70b_identical_keys_every_key():
+    """Every key's dV and every row's dQ of ranks 0 and 7 at the 131072-token shape, against
+    closed forms. With all keys of a kv head equal (k_j = k_g, the natural-order row 0), each visible key
+    gets probability 1/(pos_i + 1) in row i, so dV_j is the sum, over the rank's rows i with
+    pos_i >= kpos_j and over the G query heads of the group, of dO_i / (pos_i + 1): a suffix sum
+    over the rows in position order. dQ is 0: dQ_i = scale * k_g * sum_j dS_ij, and the dS of a
+    row sums to zero. Tolerance as for the other backward checks, 2e-2 * max(1, max |ref|)."""
+    w = synth.LLAMA31_70B_S131K
+    cp, S = w.cps[0], w.seq
+    announce(f"backward {w.name} identical keys, every key: generating inputs")
+    q, k, v = synth.workload_prefill_inputs(w)
+    do = synth.workload_prefill_grad(w)
+    qd, vd, dod = q.to(DEV), v.to(DEV), do.to(DEV)
+    k1d = k[:, :1].expand(-1, S, -1, -1).contiguous().to(DEV)
+    kp, vp = cpa.permute(k1d, cp), cpa.permute(vd, cp)
+    for rank in (0, 7):
+        announce(f"backward {w.name} identical keys, every key: rank {rank}")
+        dq, dk, dv = run_bwd_rank(qd, k1d, vd, dod, S, cp, rank, w.scale, kp, vp)
+        check_identical_keys_bwd(w, cp, rank, do, dq, dv)
+
+
+def check_identical_keys_bwd(w, cp, rank, do, dq, dv):
+    S = w.seq
+    c, G = S // (2 * cp), w.hq // w.hkv
+    perm = olb.load_balance_perm(S, cp)           # position of gathered key j
+    rows = perm[rank * 2 * c:(rank + 1) * 2 * c]  # the rank's row positions, ascending
+    assert np.all(np.diff(rows) > 0)
+    first = np.searchsorted(rows, perm, side="left")  # first of the rank's rows that sees key j
+    seen = first < 2 * c
+    do_rows = do[0, torch.from_numpy(rows)]       # [2c, Hq, Dv]
+    inv_n = torch.from_numpy(1.0 / (rows + 1.0))[:, None]
+    dv = dv[0].cpu()                              # [S, Hkv, Dv], gathered key order
+    worst = 0.0
+    for g in range(w.hkv):
+        contrib = do_rows[:, g * G:(g + 1) * G].double().sum(1) * inv_n      # [2c, Dv]
+        suffix = contrib.flip(0).cumsum(0).flip(0)                           # rows i and after
+        ref = torch.zeros((S, w.d_v), dtype=torch.float64)
+        ref[torch.from_numpy(seen)] = suffix[torch.from_numpy(first[seen])]
+        err = float((dv[:, g].double() - ref).abs().max())
+        tol = bwd_tol(ref.numpy())
+        worst = max(worst, err / tol)
+        assert err <= tol, f"dV rank {rank} kv head {g}: max err {err:.3e} > {tol:.3e}"
+    dq_max = float(dq.abs().max())
+    print(f"  every key's dV within {worst:.3f} of its bound; max |dQ| {dq_max:.3e} (exact 0)", flush=True)
+    assert dq_max <= bwd_tol(np.zeros(1))

@@ -17,6 +17,8 @@ from context_causal_attention_load_amd import synth
 from oracle import attention as oatt
 from oracle import lb_index as olb
 
+from closed_forms import bwd_tol, check_identical_keys_bwd, check_identical_keys_dk
+
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
@@ -579,11 +581,6 @@ def test_quantize_then_decode_int8():
 from oracle import backward as obw  # noqa: E402
 
 
-def bwd_tol(ref):
-    """bf16 gradients: |err| <= 2e-2 * max(1, max |ref|) (bf16 P, dS and inputs; fp32 sums)."""
-    return 2e-2 * max(1.0, float(np.abs(ref).max()))
-
-
 def run_bwd_rank(qd, kd, vd, dod, seq, cp, rank, scale, kp=None, vp=None):
     """GPU: permute the shard's Q and dO and the full K/V, forward, then backward."""
     c = seq // (2 * cp)
@@ -701,8 +698,8 @@ def test_backward_llama70b_full_size_sampled(rank):
 
 
 def test_backward_llama70b_identical_keys_every_key():
-    """Every key's dV and every row's dQ of ranks 0 and 7 at the 131072-token shape, against
-    closed forms. With all keys of a kv head equal (k_j = k_g, the natural-order row 0), each visible key
+    """Every key's dV and dK and every row's dQ of ranks 0 and 7 at the 131072-token shape,
+    against closed forms (dK: check_identical_keys_dk). With all keys of a kv head equal (k_j = k_g, the natural-order row 0), each visible key
     gets probability 1/(pos_i + 1) in row i, so dV_j is the sum, over the rank's rows i with
     pos_i >= kpos_j and over the G query heads of the group, of dO_i / (pos_i + 1): a suffix sum
     over the rows in position order. dQ is 0: dQ_i = scale * k_g * sum_j dS_ij, and the dS of a
@@ -719,29 +716,4 @@ def test_backward_llama70b_identical_keys_every_key():
         announce(f"backward {w.name} identical keys, every key: rank {rank}")
         dq, dk, dv = run_bwd_rank(qd, k1d, vd, dod, S, cp, rank, w.scale, kp, vp)
         check_identical_keys_bwd(w, cp, rank, do, dq, dv)
-
-
-def check_identical_keys_bwd(w, cp, rank, do, dq, dv):
-    S = w.seq
-    c, G = S // (2 * cp), w.hq // w.hkv
-    perm = olb.load_balance_perm(S, cp)           # position of gathered key j
-    rows = perm[rank * 2 * c:(rank + 1) * 2 * c]  # the rank's row positions, ascending
-    assert np.all(np.diff(rows) > 0)
-    first = np.searchsorted(rows, perm, side="left")  # first of the rank's rows that sees key j
-    seen = first < 2 * c
-    do_rows = do[0, torch.from_numpy(rows)]       # [2c, Hq, Dv]
-    inv_n = torch.from_numpy(1.0 / (rows + 1.0))[:, None]
-    dv = dv[0].cpu()                              # [S, Hkv, Dv], gathered key order
-    worst = 0.0
-    for g in range(w.hkv):
-        contrib = do_rows[:, g * G:(g + 1) * G].double().sum(1) * inv_n      # [2c, Dv]
-        suffix = contrib.flip(0).cumsum(0).flip(0)                           # rows i and after
-        ref = torch.zeros((S, w.d_v), dtype=torch.float64)
-        ref[torch.from_numpy(seen)] = suffix[torch.from_numpy(first[seen])]
-        err = float((dv[:, g].double() - ref).abs().max())
-        tol = bwd_tol(ref.numpy())
-        worst = max(worst, err / tol)
-        assert err <= tol, f"dV rank {rank} kv head {g}: max err {err:.3e} > {tol:.3e}"
-    dq_max = float(dq.abs().max())
-    print(f"  every key's dV within {worst:.3f} of its bound; max |dQ| {dq_max:.3e} (exact 0)", flush=True)
-    assert dq_max <= bwd_tol(np.zeros(1))
+        check_identical_keys_dk(w, cp, rank, q, v, do, dk)

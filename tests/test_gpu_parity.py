@@ -717,3 +717,21 @@ def test_backward_llama70b_identical_keys_every_key():
         dq, dk, dv = run_bwd_rank(qd, k1d, vd, dod, S, cp, rank, w.scale, kp, vp)
         check_identical_keys_bwd(w, cp, rank, do, dq, dv)
         check_identical_keys_dk(w, cp, rank, q, v, do, dk)
+
+
+def test_backward_mla_identical_keys_every_key():
+    """The DeepSeek-V3 MLA shape (Dqk 192, Dv 128, 128 kv heads), ranks 0 and 3 at cp = 4: every
+    key's dV and every row's dQ against the identical-key closed forms (dK there is covered by
+    the sampled check; its row-by-row closed form over 128 kv heads is too slow for the suite)."""
+    w = synth.DEEPSEEK_V3_MLA_S32K
+    cp, S = w.cps[0], w.seq
+    announce(f"backward {w.name} identical keys, every key: generating inputs")
+    q, k, v = synth.workload_prefill_inputs(w)
+    do = synth.workload_prefill_grad(w)
+    qd, vd, dod = q.to(DEV), v.to(DEV), do.to(DEV)
+    k1d = k[:, :1].expand(-1, S, -1, -1).contiguous().to(DEV)
+    kp, vp = cpa.permute(k1d, cp), cpa.permute(vd, cp)
+    for rank in (0, cp - 1):
+        announce(f"backward {w.name} identical keys, every key: rank {rank}")
+        dq, dk, dv = run_bwd_rank(qd, k1d, vd, dod, S, cp, rank, w.scale, kp, vp)
+        check_identical_keys_bwd(w, cp, rank, do, dq, dv)

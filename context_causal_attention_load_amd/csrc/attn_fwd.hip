@@ -9,8 +9,9 @@
 //
 // Design (bf16):
 //  * A workgroup is 8 wavefronts. It owns `hpw` query heads of one KV group and 32*8/hpw query
-//    rows; each wave owns one head and 32 rows. All waves stream the same K/V tiles (64 keys)
-//    through LDS, so one tile serves every head of the group that the workgroup holds.
+//    rows; each wave owns one head and 32 rows. All waves stream the same K/V tiles (128 keys
+//    where two stages fit in LDS, as at head dim 128; 64 at the MLA head dims) through LDS,
+//    so one tile serves every head of the group that the workgroup holds.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K (row-major
 //    in LDS) is the A operand, the Q fragment lives in registers as the B operand. In the
 //    result each lane holds 16 keys of ONE query row, so row max/sum need a single exchange

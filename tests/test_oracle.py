@@ -171,6 +171,47 @@ def test_permutation_round_trip_bit_exact(seq, cp):
     assert torch.equal(z, x)
 
 
+def _golden_rows():
+    with open(os.path.join(GOLDEN, "lb_perm_s8_cp2.txt")) as f:
+        lines = [ln for ln in f if ln.strip() and not ln.startswith("#")]
+    out = []
+    for ln in lines:
+        parts = [p.split() for p in ln.split("|")]
+        out.append((int(parts[0][0]), int(parts[0][1]), [[int(x) for x in p] for p in parts[1:]]))
+    return out
+
+
+def _check_permute_direction(permute_fn, unpermute_fn):
+    """The direction of the reference gather and scatter, pinned to the worked example and to the
+    chunk rule itself (not to the oracle's index function): permuting the token ids 0..S-1 must
+    give the shards printed on the page, rank r's window must read chunk r then chunk 2cp-1-r,
+    and scattering the page's permuted ids must give 0..S-1 back. A gather by the inverse
+    permutation (gather and scatter confused) gives 0,1,4,5,6,7,2,3 for the example."""
+    for seq, cp, shards in _golden_rows():
+        ids = torch.arange(seq, dtype=torch.int64)[None]
+        got = permute_fn(ids, seq, cp)[0].tolist()
+        assert got == [t for sh in shards for t in sh], (got, shards)
+        flat = torch.tensor([t for sh in shards for t in sh], dtype=torch.int64)[None]
+        back = unpermute_fn(flat, torch.zeros_like(flat), seq, cp)[0].tolist()
+        assert back == list(range(seq)), back
+    for seq, cp in [(48, 3), (64, 4), (4096, 8)]:
+        c = seq // (2 * cp)
+        ids = torch.arange(seq, dtype=torch.int64)[None]
+        for r in range(cp):
+            win = permute_fn(ids, seq, cp, r * 2 * c, 2 * c)[0]
+            assert torch.equal(win[:c], torch.arange(r * c, (r + 1) * c)), (seq, cp, r)
+            assert torch.equal(win[c:], torch.arange((2 * cp - 1 - r) * c, (2 * cp - r) * c)), (seq, cp, r)
+            # scattering the window alone writes exactly the two chunks' ids at their own positions
+            z = unpermute_fn(win[None], torch.full_like(ids, -1), seq, cp, r * 2 * c)[0]
+            hit = (z >= 0).nonzero().flatten()
+            assert torch.equal(z[hit], hit), (seq, cp, r)
+            assert len(hit) == 2 * c
+
+
+def test_permute_ref_direction():
+    _check_permute_direction(oatt.permute_ref, oatt.unpermute_ref)
+
+
 def test_index_rejects_bad_shapes():
     with pytest.raises(ValueError):
         olb.load_balance_perm(10, 2)
@@ -720,8 +761,25 @@ def _bwd_dv_one_head(q, k, v, do, q_pos, k_pos, scale):
     return dq, dk, dv0
 
 
+def _permute_by_inverse(x, seq, cp, row_begin=0, row_count=None):
+    # gathers with the inverse permutation (gather and scatter confused)
+    inv = olb.inverse_perm(olb.load_balance_perm(seq, cp))
+    if row_count is None:
+        row_count = seq - row_begin
+    return x[:, inv[row_begin:row_begin + row_count]]
+
+
+def _unpermute_by_inverse(x_window, dst, seq, cp, row_begin=0):
+    inv = olb.inverse_perm(olb.load_balance_perm(seq, cp))
+    out = dst.clone()
+    out[:, inv[row_begin:row_begin + x_window.shape[1]]] = x_window
+    return out
+
+
 @pytest.mark.parametrize("check", [
     lambda: _check_golden(_perm_swapped_chunk_order),
+    lambda: _check_permute_direction(_permute_by_inverse, _unpermute_by_inverse),
+    lambda: _check_permute_direction(oatt.permute_ref, _unpermute_by_inverse),
     lambda: _check_balance(_perm_unbalanced, 64, 4),
     lambda: _check_brute(_att_strict_mask, 8, 2, 2, 2, 4, 4, 3),
     lambda: _check_library(_att_no_scale, 64, 2, 4, 2, 16, 16, 3),
@@ -735,7 +793,7 @@ def _bwd_dv_one_head(q, k, v, do, q_pos, k_pos, scale):
     lambda: _check_bwd_library(_bwd_no_delta, 32, 2, 4, 2, 8, 4, 5),
     lambda: _check_bwd_finite_differences(_bwd_dk_unscaled),
     lambda: _check_bwd_library(_bwd_dv_one_head, 32, 2, 4, 2, 8, 4, 5),
-], ids=["chunk-order", "unbalanced", "strict-mask", "no-scale", "wrong-group", "mirrored-v", "decode-length",
+], ids=["chunk-order", "permute-by-inverse", "unpermute-by-inverse", "unbalanced", "strict-mask", "no-scale", "wrong-group", "mirrored-v", "decode-length",
         "merge-unweighted", "quant-ties-away", "int8-k-scale-on-v", "int8-no-k-scale", "bwd-no-delta", "bwd-dk-unscaled",
         "bwd-dv-one-head"])
 def test_planted_mistakes_are_caught(check):

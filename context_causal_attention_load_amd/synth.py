@@ -115,6 +115,36 @@ def workload_prefill_inputs(w: PrefillWorkload, seed=None):
     return prefill_inputs(w.batch, w.seq, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype, w.seed if seed is None else seed)
 
 
+# Query factors of the rising-logit inputs: powers of two, so every planted value is exact in
+# bfloat16 and a power-of-two softmax scale keeps it exact after scaling.
+RISE_Q_FACTORS = (0.125, 0.25, 0.5, 1.0, 2.0)
+
+
+def plant_rising_logits(q, k, step_tokens, step_height, q_factors=RISE_Q_FACTORS):
+    """Give the logits a staircase that rises with the key's original position (in place, on
+    natural-order CPU tensors Q [B, S, Hq, Dqk] and K [B, S, Hkv, Dqk]).
+
+    Dimension 0 of every key at position u becomes ``step_height * (u // step_tokens)`` and
+    dimension 0 of query (position t, head h) becomes ``q_factors[(t + h) % len(q_factors)]``,
+    so that dimension adds ``q_factor * step_height * (u // step_tokens)`` to the raw dot product:
+    a query's largest logit keeps growing as later keys come in, by an amount per step that
+    differs between neighbouring rows and heads. The other dimensions keep their N(0,1) draws.
+    Every planted value must be exact in the tensors' dtype (checked)."""
+    S = q.shape[1]
+    steps = torch.div(torch.arange(S, dtype=torch.int64), step_tokens, rounding_mode="floor")
+    kval = (steps * step_height).to(torch.float64)
+    if not torch.equal(kval.to(k.dtype).to(torch.float64), kval):
+        raise ValueError("planted key values are not exact in the key dtype")
+    f = torch.tensor(q_factors, dtype=torch.float64)
+    if not torch.equal(f.to(q.dtype).to(torch.float64), f):
+        raise ValueError("query factors are not exact in the query dtype")
+    hq = q.shape[2]
+    idx = (torch.arange(S)[:, None] + torch.arange(hq)[None, :]) % len(q_factors)
+    q[:, :, :, 0] = f[idx].to(q.dtype)[None]
+    k[:, :, :, 0] = kval.to(k.dtype)[None, :, None]
+    return q, k
+
+
 def decode_inputs(batch, hq, hkv, d, max_len, len_min, len_max, dtype, seed):
     """lengths [B] int32, q [B,Hq,D], k_cache / v_cache [B,Hkv,Lmax,D] (CPU tensors)."""
     gen = torch.Generator("cpu").manual_seed(seed)

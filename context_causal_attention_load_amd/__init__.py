@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     attention_bwd,
     attention_bwd_workspace_bytes,
     decode,
+    decode_noalloc,
     decode_merge,
     decode_int8,
     quantize_kv,

@@ -61,6 +61,8 @@ def load_library():
     lib.gqa_decode_attention.restype = ctypes.c_int
     lib.gqa_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                          vp, ctypes.c_size_t, vp]
+    lib.gqa_decode_attention_noalloc.restype = ctypes.c_int
+    lib.gqa_decode_attention_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
     lib.gqa_decode_merge.restype = ctypes.c_int
     lib.gqa_decode_merge.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.gqa_decode_attention_int8kv.restype = ctypes.c_int
@@ -237,6 +239,32 @@ def decode(q, k_cache, v_cache, lengths, scale=None, workspace=None, out=None, l
                                                _ptr(lse), B, Hq, Hkv, D, Lmax, _DTYPES[q.dtype], float(scale),
                                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                                _stream(q.device)))
+    return out, lse
+
+
+def decode_noalloc(q, k_cache, v_cache, lengths, out, lse=None, scale=None):
+    """decode() for callers that cannot allocate: the split partials live in the library's static
+    device scratch, and ``out`` (and ``lse``, optional) must be given, so no device memory is
+    allocated here either. Calls that overlap on one GPU race (they share the scratch)."""
+    _need_gpu(q, k_cache, v_cache, lengths, out, lse)
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and caches must share dtype float32 or bfloat16")
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, Hkv, Lmax, D) or v_cache.shape != (B, Hkv, Lmax, D):
+        raise ValueError("cache shapes do not match q")
+    if lengths.dtype != torch.int32 or lengths.shape != (B,):
+        raise ValueError("lengths must be int32 [B]")
+    if out is None:
+        raise ValueError("out must be given (this call allocates nothing)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check_buf(out, (B, Hq, D), q.dtype, "out")
+    _check_buf(lse, (B, Hq), torch.float32, "lse")
+    _check("gqa_decode_attention_noalloc",
+           load_library().gqa_decode_attention_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lengths),
+                                                       _ptr(out), _ptr(lse), B, Hq, Hkv, D, Lmax, _DTYPES[q.dtype],
+                                                       float(scale), _stream(q.device)))
     return out, lse
 
 

@@ -262,11 +262,16 @@ size_t gqa_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_
   return (size_t)batch * hq * decode_nsplit(max_len) * (size_t)(d + 2) * sizeof(float);
 }
 
-int gqa_decode_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
-                         void* o, float* lse, int32_t batch, int32_t hq, int32_t hkv, int32_t d,
-                         int32_t max_len, int32_t dtype, float softmax_scale, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  const char* where = "gqa_decode_attention";
+}  // extern "C"
+
+namespace {
+
+// Checks and launch shared by the two bf16/fp32 decode entry points: `workspace` is the caller's
+// buffer or the library's static scratch.
+int decode_checked(const char* where, const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
+                   void* o, float* lse, int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t max_len,
+                   int32_t dtype, float softmax_scale, bool noalloc, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   if (batch < 0) return fail(CPA_EINVAL, "%s: batch must be >= 0", where);
   if (hq < 1 || hkv < 1 || hq % hkv != 0)
     return fail(CPA_EINVAL, "%s: hq (%d) must be a positive multiple of hkv (%d)", where, hq, hkv);
@@ -277,17 +282,29 @@ int gqa_decode_attention(const void* q, const void* k_cache, const void* v_cache
   if (d != 64 && d != 128) return fail(CPA_ENOTSUP, "%s: head dim %d not supported (64, 128)", where, d);
   if (batch == 0) return CPA_OK;
   if ((int64_t)batch * hkv * max_len * d >= (int64_t(1) << 40)) return fail(CPA_EINVAL, "%s: cache too large", where);
-  if (!q || !k_cache || !v_cache || !lengths || !o || !workspace)
+  if (!q || !k_cache || !v_cache || !lengths || !o || (!noalloc && !workspace))
     return fail(CPA_EINVAL, "%s: null pointer", where);
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      (!noalloc && !aligned16(workspace)))
     return fail(CPA_EINVAL, "%s: q, caches, o and workspace must be 16-byte aligned", where);
   if (((uintptr_t)lengths & 3u) || (lse && ((uintptr_t)lse & 3u)))
     return fail(CPA_EINVAL, "%s: lengths and lse must be 4-byte aligned", where);
-  size_t need = gqa_decode_workspace_bytes(batch, hq, hkv, max_len, d);
-  if (workspace_bytes < need)
+  const size_t need = gqa_decode_workspace_bytes(batch, hq, hkv, max_len, d);
+  if (noalloc) {
+    if (need > kDecodeNoAllocScratchBytes)
+      return fail(CPA_EINVAL,
+                  "%s: this call needs %zu bytes of split partials (batch %d x hq %d x %d splits x (d + 2) floats), "
+                  "more than the library's static scratch of %zu bytes; use gqa_decode_attention with a workspace",
+                  where, need, batch, hq, decode_nsplit(max_len), (size_t)kDecodeNoAllocScratchBytes);
+  } else if (workspace_bytes < need) {
     return fail(CPA_EINVAL, "%s: workspace of %zu bytes, need %zu", where, workspace_bytes, need);
+  }
   int rc = check_device(where);
   if (rc) return rc;
+  if (noalloc) {
+    hipError_t e = decode_noalloc_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, where);
+  }
   DecodeArgs a;
   a.q = q;
   a.k = k_cache;
@@ -308,6 +325,25 @@ int gqa_decode_attention(const void* q, const void* k_cache, const void* v_cache
                                    : launch_decode_f32(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, where);
   return CPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_decode_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
+                         void* o, float* lse, int32_t batch, int32_t hq, int32_t hkv, int32_t d,
+                         int32_t max_len, int32_t dtype, float softmax_scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return decode_checked("gqa_decode_attention", q, k_cache, v_cache, lengths, o, lse, batch, hq, hkv, d, max_len,
+                        dtype, softmax_scale, false, workspace, workspace_bytes, stream);
+}
+
+int gqa_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* lengths,
+                                 void* o, float* lse, int32_t batch, int32_t hq, int32_t hkv, int32_t d,
+                                 int32_t max_len, int32_t dtype, float softmax_scale, void* stream) {
+  return decode_checked("gqa_decode_attention_noalloc", q, k_cache, v_cache, lengths, o, lse, batch, hq, hkv, d,
+                        max_len, dtype, softmax_scale, true, nullptr, 0, stream);
 }
 
 int gqa_decode_attention_int8kv(const void* q, const int8_t* k_codes, const int8_t* v_codes,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/cpattn.h"
+
 namespace cpattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -155,5 +157,11 @@ hipError_t launch_decode_split_merge(const int32_t* lengths, float* ws, void* o,
 // the split's max and sum (log2 units).
 constexpr int kDecodeSplitLen = 256;
 inline int decode_nsplit(int max_len) { return (max_len + kDecodeSplitLen - 1) / kDecodeSplitLen; }
+
+// Size of the file-scope device array that replaces the caller workspace in the
+// allocation-free decode call (one copy per GPU, held until the process ends).
+constexpr size_t kDecodeNoAllocScratchBytes = CPATTN_DECODE_NOALLOC_SCRATCH_BYTES;
+// Device address of that array on the current GPU (looked up once per device).
+hipError_t decode_noalloc_scratch(void** out);
 
 }  // namespace cpattn

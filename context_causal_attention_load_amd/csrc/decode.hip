@@ -18,6 +18,8 @@
 //  * The merge is a separate launch: merging inside the split kernel (last workgroup to
 //    arrive) needs a device-scope release per workgroup, which on this part writes back the
 //    whole L2 and costs far more than the second launch.
+#include <mutex>
+
 #include "common.h"
 
 namespace cpattn {
@@ -599,6 +601,36 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// ------------------------------------------------------------------------------------------
+// Device scratch of the allocation-free decode call
+// ------------------------------------------------------------------------------------------
+// gqa_decode_attention_noalloc keeps its split partials in this file-scope array instead of a
+// caller workspace. Each GPU the library runs on holds its own copy until the process ends. In
+// host code the name is only a host-side stand-in, never a device address: the address on the
+// current GPU comes from hipGetSymbolAddress, taken once per device and kept below, and only
+// that address is handed to the kernels.
+static __device__ __align__(256) char scratch[kDecodeNoAllocScratchBytes];
+
+hipError_t decode_noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) { return launch_typed<__bf16>(a, stream); }
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) { return launch_typed<float>(a, stream); }

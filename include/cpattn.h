@@ -188,6 +188,25 @@ int gqa_decode_attention(const void* q, const void* k_cache, const void* v_cache
                          int32_t dtype, float softmax_scale,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* gqa_decode_attention_noalloc: gqa_decode_attention for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, results and errors as gqa_decode_attention, minus the workspace: the split
+ * partials go to a static device array of CPATTN_DECODE_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library (one per GPU, held until the process ends; its address is looked up once per device on
+ * the first call there). The call performs no hipMalloc or hipFree and calls no allocating routine.
+ *   Limit: gqa_decode_workspace_bytes(batch, hq, hkv, max_len, d) must not exceed
+ *   CPATTN_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB: e.g. batch 24, 48 query heads, max_len 2048,
+ *   d 128 needs 4.8 MiB); larger calls return CPA_EINVAL with a message and enqueue nothing.
+ *   Every call on one GPU shares that GPU's array and leaves its partials there: calls that
+ *   overlap on one GPU (other streams, or other threads) race and give undefined results;
+ *   calls ordered on one stream are safe. */
+#define CPATTN_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int gqa_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* lengths, void* o, float* lse,
+                                 int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t max_len,
+                                 int32_t dtype, float softmax_scale, void* stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Merge of decode results over a cache split along its length ("rename context to
  * context_autoregressive", PR 1453, Description: a separate context-parallel axis for

@@ -197,6 +197,33 @@ def test_decode_argument_errors(lib, kw, status, substr):
     assert rc == status and substr in msg, (rc, msg)
 
 
+def _dec_noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lengths=FAKE, o=FAKE, lse=None, batch=24, hq=48, hkv=8, d=128, max_len=2048,
+             dtype=binding.CPA_BF16, scale=0.088)
+    a.update(kw)
+    rc = lib.gqa_decode_attention_noalloc(a["q"], a["k"], a["v"], a["lengths"], a["o"], a["lse"], a["batch"],
+                                          a["hq"], a["hkv"], a["d"], a["max_len"], a["dtype"], a["scale"], None)
+    return _status_and_message(lib, rc)
+
+
+@pytest.mark.parametrize("kw,status,substr", [
+    (dict(hq=50), binding.CPA_EINVAL, "multiple of hkv"),
+    (dict(max_len=0), binding.CPA_EINVAL, "max_len"),
+    (dict(scale=float("nan")), binding.CPA_EINVAL, "softmax_scale"),
+    (dict(d=96), binding.CPA_ENOTSUP, "head dim"),
+    (dict(o=None), binding.CPA_EINVAL, "null"),
+    (dict(q=ctypes.c_void_p(4104)), binding.CPA_EINVAL, "aligned"),
+    (dict(batch=64, hq=64, max_len=8192), binding.CPA_EINVAL, "static scratch"),
+])
+def test_decode_noalloc_argument_errors(lib, kw, status, substr):
+    rc, msg = _dec_noalloc(lib, **kw)
+    assert rc == status and substr in msg, (rc, msg)
+
+
+def test_decode_noalloc_empty_is_ok_without_device(lib):
+    assert _dec_noalloc(lib, batch=0)[0] == 0
+
+
 def _merge(lib, **kw):
     a = dict(o_parts=FAKE, lse_parts=FAKE, o=FAKE, lse=None, parts=4, batch=24, hq=48, d=128, dtype=binding.CPA_BF16)
     a.update(kw)

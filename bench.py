@@ -342,9 +342,22 @@ def bench_decode_int8(w, iters, dev, copies=6):
                 b2b_gbs=alg / (b2b * 1e-3) / 1e9)
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, cp, rank, n_rows, seed=0):
     """Time the CPU fp64 oracle (as it is) on a row sample of one rank: its permutes of the
-    rank's windows plus attention for ``n_rows`` query rows over all heads."""
+    rank's windows plus attention for the sampled query rows over all heads. The sample is
+    stratified: the first and last 8 rows of both chunks, the rest drawn uniformly from the shard.
+    Reports useful TFLOP/s on the sampled rows' causal pairs and, from that rate, the time the
+    oracle would take for the whole shard (labelled extrapolated)."""
     import numpy as np
 
     from context_causal_attention_load_amd import synth
@@ -354,7 +367,8 @@ def cpu_baseline(w, cp, rank, n_rows, seed=0):
     q, k, v = synth.workload_prefill_inputs(w)
     S, c = w.seq, w.seq // (2 * cp)
     rng = np.random.default_rng(seed)
-    rows = np.unique(rng.integers(0, 2 * c, n_rows))
+    edge = [x for base in (0, c) for x in list(range(base, base + 8)) + list(range(base + c - 8, base + c))]
+    rows = np.unique(np.concatenate([np.array(edge), rng.integers(0, 2 * c, max(0, n_rows - len(edge)))]))
     pos = olb.shard_positions(S, cp, rank)
     t0 = time.perf_counter()
     qs = oatt.permute_ref(q, S, cp, rank * 2 * c, 2 * c)[:, rows]
@@ -364,10 +378,15 @@ def cpu_baseline(w, cp, rank, n_rows, seed=0):
     dt = time.perf_counter() - t0
     pairs = int((pos[rows] + 1).sum())
     flops = 2.0 * pairs * w.hq * (w.d_qk + w.d_v) * w.batch
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=torch.get_num_threads(), kind="oracle",
-                sample=(f"{len(rows)} random query rows (all {w.hq} heads) of rank {rank} at S={S}, cp={cp}: "
-                        f"oracle permutes of Q window and full K/V plus fp64 attention, {dt:.1f} s, "
-                        f"{flops / 1e12:.3f} useful TFLOP"),
+    rate = flops / dt
+    full = useful_flops(S, cp, w.hq, w.d_qk, w.d_v, w.batch)
+    threads = torch.get_num_threads()
+    return dict(value=rate / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=(f"{len(rows)} query rows of rank {rank} at S={S}, cp={cp} (first/last 8 rows of both chunks "
+                        f"plus uniform random rows), all {w.hq} heads: oracle permutes of the Q window and the full "
+                        f"K/V plus fp64 attention, {dt:.1f} s for {flops / 1e12:.3f} useful TFLOP"),
+                extrapolated_full_shard_s=round(full / rate, 1),
+                cpu_model=_cpu_model(), torch_threads=threads, affinity_cores=len(os.sched_getaffinity(0)),
                 seconds=dt)
 
 
@@ -377,7 +396,7 @@ def main():
     ap.add_argument("--steps", type=int, default=24)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-iters", type=int, default=200)
-    ap.add_argument("--cpu-rows", type=int, default=320)
+    ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true",

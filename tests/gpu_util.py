@@ -40,6 +40,40 @@ def sample_rows(c, n_random, seed):
     return np.unique(np.array(edge + rnd, dtype=np.int64))
 
 
+def stratified_rows(c, per_class, seed, block=32, edge=8):
+    """Rows of a 2c-row shard for a sampled full-size check: the first and last ``edge`` rows of
+    both chunks, plus ``per_class`` seeded rows for every position inside a 32-row block (the
+    kernels' row blocks), drawn from different blocks across the whole shard."""
+    n = 2 * c
+    rows = set()
+    for base in (0, c):
+        rows.update(range(base, base + min(edge, c)))
+        rows.update(range(max(base, base + c - edge), base + c))
+    rng = np.random.default_rng(seed)
+    nblk = (n + block - 1) // block
+    for k in range(min(block, n)):
+        cand = np.arange(k, n, block)
+        take = min(per_class, len(cand))
+        rows.update(rng.choice(cand, take, replace=False).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def describe_rows(rows, c):
+    """One line naming the checked rows: count, per-chunk counts, block-position coverage and the
+    rows themselves as ranges."""
+    rows = np.asarray(rows)
+    spans, start = [], rows[0]
+    for a, b in zip(rows[:-1], rows[1:]):
+        if b != a + 1:
+            spans.append((start, a))
+            start = b
+    spans.append((start, rows[-1]))
+    txt = ",".join(f"{a}" if a == b else f"{a}-{b}" for a, b in spans)
+    classes = len(set((rows % 32).tolist()))
+    return (f"{len(rows)} rows ({int((rows < c).sum())} in the lower chunk, {int((rows >= c).sum())} in the upper), "
+            f"{classes}/32 block positions: {txt}")
+
+
 class Prefill:
     """Natural-order inputs on host and device, permuted on the device by the library; the
     oracle permutes the host copies itself. ``plant`` (optional) edits the host inputs in place

@@ -18,7 +18,8 @@ from oracle import attention as oatt
 from oracle import lb_index as olb
 
 from closed_forms import bwd_tol, check_identical_keys_bwd, check_identical_keys_dk
-from gpu_util import DEV, TOL, Prefill, announce, assert_close, check_rank, sample_rows
+from gpu_util import (DEV, TOL, Prefill, announce, assert_close, check_rank, describe_rows, sample_rows,
+                      stratified_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -194,15 +195,28 @@ def test_attention_contiguous_shards_llama7b():
         assert_close(lse[:, :, pick].cpu().numpy(), L_ref, TOL[pf.dtype], f"contiguous LSE r={r}")
 
 
-FULL_CASES = [(w, cp, r) for w in (synth.LLAMA2_7B_S8K, synth.DEEPSEEK_V3_MLA_S32K, synth.LLAMA31_70B_S131K)
+def test_attention_mla_rank0_every_row():
+    """Every row and head of rank 0 at the DeepSeek-V3 MLA size (S 32768, cp 4: 8192 rows x 128
+    heads, Dqk 192, Dv 128). Rank 0 holds both the shortest chunk (positions 0..4095) and the
+    longest (28672..32767)."""
+    w = synth.DEEPSEEK_V3_MLA_S32K
+    pf = full_workload(w)
+    check_rank(pf, w.cps[0], 0, rows=None, tag=w.name)
+
+
+FULL_CASES = [(w, cp, r) for w in (synth.DEEPSEEK_V3_MLA_S32K, synth.LLAMA31_70B_S131K)
               for cp in w.cps for r in range(cp)]
 
 
 @pytest.mark.parametrize("w,cp,rank", FULL_CASES, ids=[f"{w.name}-cp{cp}-r{r}" for w, cp, r in FULL_CASES])
-def test_attention_full_size_sampled(w, cp, rank):
+def test_attention_full_size_stratified(w, cp, rank):
+    """Random-data parity at the DeepSeek-V3 MLA (cp 4) and Llama3.1-70B (cp 8) sizes, every rank:
+    the first and last 8 rows of both chunks plus 16 seeded rows for each of the 32 positions in a
+    32-row block (about 540 rows), every head, element by element against the oracle."""
     pf = full_workload(w)
     c = w.seq // (2 * cp)
-    rows = sample_rows(c, 16 if w.seq >= 100000 else 24, seed=1000 * cp + rank)
+    rows = stratified_rows(c, 16, seed=1000 * cp + rank)
+    print(f"  checked rows of rank {rank}: {describe_rows(rows, c)}", flush=True)
     check_rank(pf, cp, rank, rows=rows, tag=w.name)
 
 

@@ -265,14 +265,18 @@ def other_configs_ms(dev, iters=5):
             kp, vp = cpa.permute(kd, cp), cpa.permute(vd, cp)
             o = torch.empty((w.batch, 2 * c, w.hq, w.d_v), dtype=w.dtype, device=dev)
             lse = torch.empty((w.batch, w.hq, 2 * c), dtype=torch.float32, device=dev)
+            # the split of heavy row blocks (small grids) gets its workspace before timing
+            need = max(cpa.attention_fwd_workspace_bytes(w.batch, w.seq, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype, cp, r)
+                       for r in range(cp))
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
             ms = []
             for r in range(cp):
                 qs = cpa.permute(qd, cp, row_begin=r * 2 * c, row_count=2 * c)
-                cpa.attention_fwd(qs, kp, vp, cp, r, scale=w.scale, out=o, lse=lse)
+                cpa.attention_fwd(qs, kp, vp, cp, r, scale=w.scale, out=o, lse=lse, workspace=ws)
                 evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
                 for a, b in evs:
                     a.record()
-                    cpa.attention_fwd(qs, kp, vp, cp, r, scale=w.scale, out=o, lse=lse)
+                    cpa.attention_fwd(qs, kp, vp, cp, r, scale=w.scale, out=o, lse=lse, workspace=ws)
                     b.record()
                 torch.cuda.synchronize()
                 ms.append(sorted(a.elapsed_time(b) for a, b in evs)[iters // 2])
@@ -280,6 +284,7 @@ def other_configs_ms(dev, iters=5):
             avg = sum(ms) / len(ms)
             tf = flops / (avg * 1e-3) / 1e12
             out.append({"workload": f"{w.name} cp={cp}", "ms_per_rank": [round(x, 3) for x in ms],
+                        "rank_max_over_mean": round(max(ms) / avg, 4), "heavy_row_blocks_split": need > 0,
                         "useful_flop_per_rank": flops, "tflops": round(tf, 1),
                         "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         del qd, kd, vd

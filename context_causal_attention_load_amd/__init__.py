@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     permute,
     unpermute,
     attention_fwd,
+    attention_fwd_workspace_bytes,
     attention_bwd,
     attention_bwd_workspace_bytes,
     decode,

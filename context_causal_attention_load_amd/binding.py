@@ -56,6 +56,11 @@ def load_library():
     lib.cp_attention_fwd.restype = ctypes.c_int
     lib.cp_attention_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                      f32, i32, i32, vp]
+    lib.cp_attention_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.cp_attention_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.cp_attention_fwd_ws.restype = ctypes.c_int
+    lib.cp_attention_fwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                        f32, i32, i32, vp, ctypes.c_size_t, vp]
     lib.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.gqa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.gqa_decode_attention.restype = ctypes.c_int
@@ -176,12 +181,21 @@ def unpermute(x, cp, seq, dim=1, row_begin=0, out=None):
 
 # ---------------------------------------------------------------------------- attention
 
+def attention_fwd_workspace_bytes(batch, seq, hq, hkv, d_qk, d_v, dtype, cp, rank):
+    """Workspace bytes the forward uses to split heavy row blocks of the rank's own shard (0: none)."""
+    return int(load_library().cp_attention_fwd_workspace_bytes(batch, seq, hq, hkv, d_qk, d_v, _DTYPES[dtype], cp,
+                                                                rank))
+
+
 def attention_fwd(q_shard, k, v, cp, rank, q_positions=None, scale=None, out=None, lse=None,
-                  want_lse=True):
+                  want_lse=True, workspace=None, split=True):
     """One rank's causal GQA attention over all-gathered K/V in load-balanced order.
 
     q_shard [B, Sq, Hq, Dqk]; k [B, S, Hkv, Dqk]; v [B, S, Hkv, Dv]; q_positions int32 [Sq] on
     the GPU or None (the rank's own shard). Returns (O [B, Sq, Hq, Dv], LSE [B, Hq, Sq] fp32).
+    With ``split`` (the default) a shape whose grid is too small to balance itself gets a
+    workspace (``workspace``, or a new one) and the library splits its heavy row blocks;
+    ``split=False`` calls cp_attention_fwd, which never splits.
     """
     _need_gpu(q_shard, k, v, q_positions, out, lse)
     if q_shard.dtype not in _DTYPES or k.dtype != q_shard.dtype or v.dtype != q_shard.dtype:
@@ -200,6 +214,20 @@ def attention_fwd(q_shard, k, v, cp, rank, q_positions=None, scale=None, out=Non
         out = torch.empty((B, Sq, Hq, Dv), dtype=q_shard.dtype, device=q_shard.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q_shard.device)
+    ws_need = 0
+    if split and q_positions is None:
+        ws_need = attention_fwd_workspace_bytes(B, S, Hq, Hkv, Dqk, Dv, q_shard.dtype, cp, rank)
+    if ws_need > 0:
+        _need_gpu(workspace)
+        if workspace is None:
+            workspace = torch.empty(ws_need, dtype=torch.uint8, device=q_shard.device)
+        _check("cp_attention_fwd_ws",
+               load_library().cp_attention_fwd_ws(_ptr(q_shard), _ptr(k), _ptr(v), _ptr(q_positions), _ptr(out),
+                                                  _ptr(lse), B, S, Sq, Hq, Hkv, Dqk, Dv, _DTYPES[q_shard.dtype],
+                                                  float(scale), cp, rank, _ptr(workspace),
+                                                  workspace.numel() * workspace.element_size(),
+                                                  _stream(q_shard.device)))
+        return out, lse
     _check("cp_attention_fwd",
            load_library().cp_attention_fwd(_ptr(q_shard), _ptr(k), _ptr(v), _ptr(q_positions), _ptr(out),
                                            _ptr(lse), B, S, Sq, Hq, Hkv, Dqk, Dv, _DTYPES[q_shard.dtype],

@@ -133,20 +133,20 @@ int cp_load_balance_unpermute(const void* src, void* dst, int64_t outer, int64_t
                         row_count, true, stream);
 }
 
-int cp_attention_fwd(const void* q_shard, const void* k, const void* v, const int32_t* q_positions,
-                     void* o, float* lse, int32_t batch, int32_t seq, int32_t sq, int32_t hq, int32_t hkv,
-                     int32_t d_qk, int32_t d_v, int32_t dtype, float softmax_scale, int32_t cp,
-                     int32_t rank, void* stream) {
-  const char* where = "cp_attention_fwd";
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the forward calls and the workspace query: CPA_OK or the failing status.
+int fwd_shape_checks(const char* where, int32_t batch, int32_t seq, int32_t sq, int32_t hq, int32_t hkv,
+                     int32_t d_qk, int32_t d_v, int32_t dtype, int32_t cp, int32_t rank, bool positions_given) {
   int rc = check_lb(where, seq, cp);
   if (rc) return rc;
   if (rank < 0 || rank >= cp) return fail(CPA_EINVAL, "%s: rank %d outside [0, %d)", where, rank, cp);
   if (batch < 0 || sq < 0) return fail(CPA_EINVAL, "%s: batch and sq must be >= 0", where);
   if (hq < 1 || hkv < 1 || hq % hkv != 0)
     return fail(CPA_EINVAL, "%s: hq (%d) must be a positive multiple of hkv (%d)", where, hq, hkv);
-  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
-    return fail(CPA_EINVAL, "%s: softmax_scale must be finite and > 0", where);
-  if (!q_positions && sq != seq / cp)
+  if (!positions_given && sq != seq / cp)
     return fail(CPA_EINVAL, "%s: without q_positions, sq (%d) must equal seq/cp (%d)", where, sq, seq / cp);
   if (dtype != CPA_F32 && dtype != CPA_BF16) return fail(CPA_EINVAL, "%s: unknown dtype %d", where, dtype);
   bool supported = dtype == CPA_BF16 ? ((d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) ||
@@ -157,15 +157,12 @@ int cp_attention_fwd(const void* q_shard, const void* k, const void* v, const in
   const int64_t elt = dtype == CPA_BF16 ? 2 : 4;
   if ((int64_t)batch * seq * hkv * d_qk * elt >= (int64_t(1) << 40))
     return fail(CPA_EINVAL, "%s: tensor too large", where);
-  if (batch == 0 || sq == 0) return CPA_OK;
-  if (!q_shard || !k || !v || !o) return fail(CPA_EINVAL, "%s: null tensor pointer", where);
-  if (!aligned16(q_shard) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(CPA_EINVAL, "%s: q, k, v and o must be 16-byte aligned", where);
-  if (lse && ((uintptr_t)lse & 3u)) return fail(CPA_EINVAL, "%s: lse must be 4-byte aligned", where);
-  if (q_positions && ((uintptr_t)q_positions & 3u))
-    return fail(CPA_EINVAL, "%s: q_positions must be 4-byte aligned", where);
-  rc = check_device(where);
-  if (rc) return rc;
+  return CPA_OK;
+}
+
+AttnArgs fwd_args(const void* q_shard, const void* k, const void* v, const int32_t* q_positions, void* o, float* lse,
+                  int32_t batch, int32_t seq, int32_t sq, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
+                  float softmax_scale, int32_t cp, int32_t rank) {
   AttnArgs a;
   a.q = q_shard;
   a.k = k;
@@ -183,10 +180,66 @@ int cp_attention_fwd(const void* q_shard, const void* k, const void* v, const in
   a.cp = cp;
   a.rank = rank;
   a.scale = softmax_scale;
+  return a;
+}
+
+int fwd_checked(const char* where, const void* q_shard, const void* k, const void* v, const int32_t* q_positions,
+                void* o, float* lse, int32_t batch, int32_t seq, int32_t sq, int32_t hq, int32_t hkv, int32_t d_qk,
+                int32_t d_v, int32_t dtype, float softmax_scale, int32_t cp, int32_t rank, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int rc = fwd_shape_checks(where, batch, seq, sq, hq, hkv, d_qk, d_v, dtype, cp, rank, q_positions != nullptr);
+  if (rc) return rc;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(CPA_EINVAL, "%s: softmax_scale must be finite and > 0", where);
+  if (batch == 0 || sq == 0) return CPA_OK;
+  if (!q_shard || !k || !v || !o) return fail(CPA_EINVAL, "%s: null tensor pointer", where);
+  if (!aligned16(q_shard) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(CPA_EINVAL, "%s: q, k, v and o must be 16-byte aligned", where);
+  if (lse && ((uintptr_t)lse & 3u)) return fail(CPA_EINVAL, "%s: lse must be 4-byte aligned", where);
+  if (q_positions && ((uintptr_t)q_positions & 3u))
+    return fail(CPA_EINVAL, "%s: q_positions must be 4-byte aligned", where);
+  if (workspace && !aligned16(workspace)) return fail(CPA_EINVAL, "%s: workspace must be 16-byte aligned", where);
+  rc = check_device(where);
+  if (rc) return rc;
+  AttnArgs a = fwd_args(q_shard, k, v, q_positions, o, lse, batch, seq, sq, hq, hkv, d_qk, d_v, softmax_scale, cp,
+                        rank);
+  a.ws = workspace;
+  a.ws_bytes = workspace ? workspace_bytes : 0;
   hipError_t e = dtype == CPA_BF16 ? launch_attn_fwd_bf16(a, static_cast<hipStream_t>(stream))
                                    : launch_attn_fwd_f32(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, where);
   return CPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cp_attention_fwd(const void* q_shard, const void* k, const void* v, const int32_t* q_positions, void* o,
+                     float* lse, int32_t batch, int32_t seq, int32_t sq, int32_t hq, int32_t hkv, int32_t d_qk,
+                     int32_t d_v, int32_t dtype, float softmax_scale, int32_t cp, int32_t rank, void* stream) {
+  return fwd_checked("cp_attention_fwd", q_shard, k, v, q_positions, o, lse, batch, seq, sq, hq, hkv, d_qk, d_v,
+                     dtype, softmax_scale, cp, rank, nullptr, 0, stream);
+}
+
+size_t cp_attention_fwd_workspace_bytes(int32_t batch, int32_t seq, int32_t hq, int32_t hkv, int32_t d_qk,
+                                        int32_t d_v, int32_t dtype, int32_t cp, int32_t rank) {
+  if (cp < 1 || seq < 1 || seq % (2 * (int64_t)cp) != 0) return 0;
+  if (fwd_shape_checks("cp_attention_fwd_workspace_bytes", batch, seq, seq / cp, hq, hkv, d_qk, d_v, dtype, cp,
+                       rank, false) != CPA_OK)
+    return 0;
+  if (dtype != CPA_BF16 || batch == 0) return 0;
+  AttnArgs a = fwd_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, batch, seq, seq / cp, hq, hkv, d_qk,
+                        d_v, 1.f, cp, rank);
+  return attn_fwd_workspace_bytes(a);
+}
+
+int cp_attention_fwd_ws(const void* q_shard, const void* k, const void* v, const int32_t* q_positions, void* o,
+                        float* lse, int32_t batch, int32_t seq, int32_t sq, int32_t hq, int32_t hkv, int32_t d_qk,
+                        int32_t d_v, int32_t dtype, float softmax_scale, int32_t cp, int32_t rank, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return fwd_checked("cp_attention_fwd_ws", q_shard, k, v, q_positions, o, lse, batch, seq, sq, hq, hkv, d_qk, d_v,
+                     dtype, softmax_scale, cp, rank, workspace, workspace_bytes, stream);
 }
 
 size_t cp_attention_bwd_workspace_bytes(int32_t batch, int32_t sq, int32_t hq) {

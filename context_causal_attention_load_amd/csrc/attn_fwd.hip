@@ -34,6 +34,8 @@
 //  * Workgroup order is XCD-aware and heavy-first: consecutive work items (same KV head,
 //    neighbouring row blocks) go to the same XCD so they share its L2, and row blocks with the
 //    latest positions (most keys) start first.
+#include <algorithm>
+
 #include "attn_tiles.h"
 
 namespace cpattn {
@@ -109,7 +111,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   const char* vbase = vg + (int64_t)w.b * p.S * kv_row_bytes_v + (int64_t)w.g * DV * 2;
 
   const int c = p.c;
-  const int imax = min(qmax / c, 2 * p.cp - 1);
+
+  // the row block's visible key tiles, or the piece of them this workgroup owns
+  const int tpc = (c + C::BK - 1) / C::BK;
+  int t_beg = 0, t_end = visible_tiles(qmax, c, p.cp, C::BK);
+  if (w.piece >= 0) {
+    const int n = p.piece_cnt[w.piece], i = p.piece_idx[w.piece];
+    const int T = t_end;
+    t_beg = i * T / n;
+    t_end = (i + 1) * T / n;
+  }
 
   // DMA slots: wave-instruction (u, wave) fills LDS bytes [1024*(u*kWaves + wave), +1024) of a
   // tile, lane l at +16*l; the lane loads whichever (row, chunk) the swizzle puts there. For a
@@ -169,8 +180,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
 
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  TileCursor tc{0, 0};
-  dma_tile(tc, 0);
+  TileCursor tc{t_beg / tpc, (t_beg % tpc) * C::BK};
+  if (t_beg < t_end) dma_tile(tc, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int buf = 0;
@@ -182,10 +193,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
   const int tr_e = (lane % 16) / 4;
   const int tr_q = lane % 4;
 
-  while (tc.chunk <= imax) {
+  for (int t = t_beg; t < t_end; ++t) {
     TileCursor nx = tc;
     next_tile<C::BK>(nx, c, qmax);
-    const bool has_next = nx.chunk <= imax;
+    const bool has_next = t + 1 < t_end;
     if (has_next) dma_tile(nx, buf ^ 1);  // that stage was last read in the previous iteration
 
     const char* kb = lds + buf * C::STAGE;
@@ -313,8 +324,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     tc = nx;
   }
 
-  // ---- epilogue: O = O / l, LSE = (m + log2 l) * ln 2
   const float l_tot = wave_sum32(l_part);
+  if (w.piece >= 0 && p.piece_slot[w.piece] >= 0) {
+    // ---- one piece of a split row block: unnormalised O, running max and row sum
+    if (my_row < p.Sq) {
+      const int lrow = my_row - w.row_blk * p.bm;
+      const int lhead = wave / p.wpr;
+      const int64_t slot = (int64_t)w.unit * p.n_slots + p.piece_slot[w.piece];
+      float* po = p.part_o + ((slot * p.bm + lrow) * p.hpw + lhead) * DV;
+#pragma unroll
+      for (int mv = 0; mv < C::MV; ++mv)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+          *reinterpret_cast<f32x4*>(po + 32 * mv + 8 * a4 + 4 * hl) =
+              f32x4{oacc[mv][a4 * 4], oacc[mv][a4 * 4 + 1], oacc[mv][a4 * 4 + 2], oacc[mv][a4 * 4 + 3]};
+      if (hl == 0) {
+        float* pml = p.part_ml + ((slot * p.hpw + lhead) * p.bm + lrow) * 2;
+        pml[0] = m_run;
+        pml[1] = l_tot;
+      }
+    }
+    return;
+  }
+
+  // ---- epilogue: O = O / l, LSE = (m + log2 l) * ln 2
   const float inv_l = 1.f / l_tot;
   if (my_row < p.Sq) {
     __bf16* og = static_cast<__bf16*>(p.o) + (((int64_t)w.b * p.Sq + my_row) * p.Hq + head) * DV;
@@ -532,12 +565,155 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(FwdParams p) 
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Key-range split of heavy row blocks
+// ------------------------------------------------------------------------------------------
+// A rank's time is that of its busiest compute unit. With at least two work items per CU the
+// heavy-first order evens the CUs out; below that (the 8192-token shape at cp = 4 has one 256-row
+// block per CU, and its heaviest block sees 64 key tiles against 33 on average) the heaviest
+// row block sets the time. There the visible key tiles of each row block are cut into pieces of
+// about the same size, each piece a work item; pieces of a cut row block write unnormalised
+// partials and a merge kernel combines them by their running maxima (as the decode does).
+constexpr int kSplitBelowItems = 512;   // plan a split only for grids with fewer work items
+constexpr int kSplitTargetItems = 256;  // pieces no smaller than the grid's tiles per CU
+constexpr int kSplitMinTiles = 8;       // no piece below this many key tiles
+
+struct SplitPlan {
+  int n_pieces = 0, n_slots = 0, n_split = 0;
+  unsigned char rb[kSplitMaxPieces], idx[kSplitMaxPieces], cnt[kSplitMaxPieces];
+  signed char slot[kSplitMaxPieces];
+  unsigned char srb[kSplitMaxRb], sslot[kSplitMaxRb], scnt[kSplitMaxRb];  // cut row blocks
+};
+
+int bf16_tile_keys(int d_qk, int d_v) { return (2 * 128 * (d_qk + d_v) * 2 <= 128 * 1024) ? 128 : 64; }
+
+// The plan needs the rows' positions on the host, so it is made only for the rank's own shard
+// (positions from cp and rank).
+bool plan_split(const AttnArgs& a, const FwdParams& p, SplitPlan& sp) {
+  if (a.q_pos || p.n_items >= kSplitBelowItems || p.nrb > kSplitMaxRb) return false;
+  const int bk = bf16_tile_keys(a.d_qk, a.d_v);
+  int T[kSplitMaxRb];
+  int64_t total = 0;
+  for (int rb = 0; rb < p.nrb; ++rb) {
+    const int last_row = std::min(p.Sq, (rb + 1) * p.bm) - 1;
+    const int qmax = (int)std::min<int64_t>(lb_src((int64_t)p.rank * 2 * p.c + last_row, p.c, p.cp), p.S - 1);
+    T[rb] = visible_tiles(qmax, p.c, p.cp, bk);
+    total += T[rb];
+  }
+  const int64_t units = (int64_t)p.B * p.Hkv * p.nhs;
+  const int tau = (int)std::max<int64_t>(kSplitMinTiles, (total * units + kSplitTargetItems - 1) / kSplitTargetItems);
+  int k = 0, slot = 0;
+  for (int rb = p.nrb - 1; rb >= 0; --rb) {  // heaviest (latest positions) first
+    const int n = std::max(1, std::min((T[rb] + tau - 1) / tau, 127));
+    if (k + n > kSplitMaxPieces) return false;
+    for (int i = 0; i < n; ++i, ++k) {
+      sp.rb[k] = (unsigned char)rb;
+      sp.idx[k] = (unsigned char)i;
+      sp.cnt[k] = (unsigned char)n;
+      sp.slot[k] = (signed char)(n > 1 ? slot + i : -1);
+    }
+    if (n > 1) {
+      if (slot + n > 127) return false;
+      sp.srb[sp.n_split] = (unsigned char)rb;
+      sp.sslot[sp.n_split] = (unsigned char)slot;
+      sp.scnt[sp.n_split] = (unsigned char)n;
+      ++sp.n_split;
+      slot += n;
+    }
+  }
+  if (sp.n_split == 0) return false;
+  sp.n_pieces = k;
+  sp.n_slots = slot;
+  return true;
+}
+
+size_t split_workspace_bytes(const FwdParams& p, const SplitPlan& sp, int d_v) {
+  const size_t units = (size_t)p.B * p.Hkv * p.nhs;
+  return units * sp.n_slots * ((size_t)p.bm * p.hpw * d_v + (size_t)p.hpw * p.bm * 2) * sizeof(float);
+}
+
+struct SplitMergeParams {
+  const float* part_o;
+  const float* part_ml;
+  void* o;
+  float* lse;
+  int Sq, Hq, Hkv, G, hpw, bm, nhs, n_slots, n_split;
+  unsigned char srb[kSplitMaxRb], sslot[kSplitMaxRb], scnt[kSplitMaxRb];
+};
+
+// Block (unit, cut row block, head of the slice, group of rows); thread (row, 4 dims):
+// M = max_i m_i, w_i = 2^(m_i - M), O = sum_i w_i o_i / sum_i w_i l_i, LSE = (M + log2 L) ln 2.
+// A piece whose keys all follow a row's position has m = -inf, l = 0 and o = 0: weight 0.
+template <int DV>
+__global__ __launch_bounds__(256) void attn_fwd_split_merge_kernel(SplitMergeParams m) {
+  constexpr int TPR = DV / 4;
+  constexpr int RPB = 256 / TPR;
+  int bid = blockIdx.x;
+  const int rgs = (m.bm + RPB - 1) / RPB;
+  const int rg = bid % rgs;
+  bid /= rgs;
+  const int lh = bid % m.hpw;
+  bid /= m.hpw;
+  const int j = bid % m.n_split;
+  const int unit = bid / m.n_split;
+  const int lrow = rg * RPB + threadIdx.x / TPR;
+  const int dq = threadIdx.x % TPR;
+  const int row = m.srb[j] * m.bm + lrow;
+  if (lrow >= m.bm || row >= m.Sq) return;
+  const int hs = unit % m.nhs, bg = unit / m.nhs;
+  const int g = bg % m.Hkv, b = bg / m.Hkv;
+  const int head = g * m.G + hs * m.hpw + lh;
+  const int n = m.scnt[j];
+  const int64_t slot0 = (int64_t)unit * m.n_slots + m.sslot[j];
+  float M = -INFINITY;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, m.part_ml[(((slot0 + i) * m.hpw + lh) * m.bm + lrow) * 2]);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < n; ++i) {
+    const float* ml = m.part_ml + (((slot0 + i) * m.hpw + lh) * m.bm + lrow) * 2;
+    const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);
+    L = __builtin_fmaf(wgt, ml[1], L);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(m.part_o + (((slot0 + i) * m.bm + lrow) * m.hpw + lh) * DV + 4 * dq);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wgt, o[e], acc[e]);
+  }
+  const float inv = 1.f / L;
+  bf16x4 ov;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[e] * inv);
+  *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(m.o) + (((int64_t)b * m.Sq + row) * m.Hq + head) * DV + 4 * dq) = ov;
+  if (m.lse && dq == 0) m.lse[((int64_t)b * m.Hq + head) * m.Sq + row] = (M + __builtin_amdgcn_logf(L)) * kLn2;
+}
+
 }  // namespace
+
+size_t attn_fwd_workspace_bytes(const AttnArgs& a) {
+  FwdParams p = make_params(a);
+  SplitPlan sp;
+  if (p.n_items == 0 || !plan_split(a, p, sp)) return 0;
+  return split_workspace_bytes(p, sp, a.d_v);
+}
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
   FwdParams p = make_params(a);
   if (p.n_items == 0) return hipSuccess;
-  dim3 grid(p.per_xcd * kNumXcd), block(kThreads);
+  SplitPlan sp;
+  const bool split = a.ws && plan_split(a, p, sp) && a.ws_bytes >= split_workspace_bytes(p, sp, a.d_v);
+  if (split) {
+    p.n_pieces = sp.n_pieces;
+    p.n_slots = sp.n_slots;
+    p.part_o = static_cast<float*>(a.ws);
+    p.part_ml = p.part_o + (size_t)p.B * p.Hkv * p.nhs * sp.n_slots * p.bm * p.hpw * a.d_v;
+    for (int k = 0; k < sp.n_pieces; ++k) {
+      p.piece_rb[k] = sp.rb[k];
+      p.piece_idx[k] = sp.idx[k];
+      p.piece_cnt[k] = sp.cnt[k];
+      p.piece_slot[k] = sp.slot[k];
+    }
+    p.per_xcd = (p.B * p.Hkv + kNumXcd - 1) / kNumXcd;  // (batch, kv head) pairs per XCD
+    p.n_items = p.per_xcd * p.nhs * sp.n_pieces;         // workgroups per XCD
+  }
+  dim3 grid((split ? p.n_items : p.per_xcd) * kNumXcd), block(kThreads);
   if (a.d_qk == 128 && a.d_v == 128) {
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 128>), grid, block, 0, stream, p);
   } else if (a.d_qk == 64 && a.d_v == 64) {
@@ -546,6 +722,33 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<192, 128>), grid, block, 0, stream, p);
   } else {
     return hipErrorInvalidValue;
+  }
+  if (split) {
+    SplitMergeParams m;
+    m.part_o = p.part_o;
+    m.part_ml = p.part_ml;
+    m.o = a.o;
+    m.lse = a.lse;
+    m.Sq = p.Sq;
+    m.Hq = p.Hq;
+    m.Hkv = p.Hkv;
+    m.G = p.G;
+    m.hpw = p.hpw;
+    m.bm = p.bm;
+    m.nhs = p.nhs;
+    m.n_slots = sp.n_slots;
+    m.n_split = sp.n_split;
+    for (int j = 0; j < sp.n_split; ++j) {
+      m.srb[j] = sp.srb[j];
+      m.sslot[j] = sp.sslot[j];
+      m.scnt[j] = sp.scnt[j];
+    }
+    const int rpb = 256 / (a.d_v / 4);
+    const int64_t blocks = (int64_t)p.B * p.Hkv * p.nhs * sp.n_split * p.hpw * ((p.bm + rpb - 1) / rpb);
+    if (a.d_v == 128)
+      hipLaunchKernelGGL(attn_fwd_split_merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, m);
+    else
+      hipLaunchKernelGGL(attn_fwd_split_merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, m);
   }
   return hipGetLastError();
 }

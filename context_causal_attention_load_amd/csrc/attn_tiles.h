@@ -17,6 +17,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
 
+// Key-range split of the forward's heavy row blocks (small grids only): a plan lists, for each
+// (batch, kv head, head slice) unit, its pieces heaviest first; a piece is a range of a row
+// block's visible key tiles. Row blocks cut into several pieces write partials to the caller's
+// workspace and a merge kernel combines them.
+constexpr int kSplitMaxPieces = 96;
+constexpr int kSplitMaxRb = 64;
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -27,6 +34,14 @@ struct FwdParams {
   int B, S, Sq, Hq, Hkv, G, cp, c, rank;
   int hpw, wpr, bm, nrb, nhs, n_items, per_xcd;
   float scale_log2;
+  // split plan (n_pieces == 0: one item per row block, no partials)
+  int n_pieces, n_slots;
+  float* part_o;   // [unit, slot, bm rows, hpw heads, Dv] unnormalised outputs
+  float* part_ml;  // [unit, slot, hpw heads, bm rows, 2] running max (log2 units) and row sum
+  unsigned char piece_rb[kSplitMaxPieces];   // row block of each piece
+  unsigned char piece_idx[kSplitMaxPieces];  // index of the piece within its row block
+  unsigned char piece_cnt[kSplitMaxPieces];  // pieces of that row block
+  signed char piece_slot[kSplitMaxPieces];   // partial slot, -1 when the row block is not split
 };
 
 template <int CH>
@@ -61,23 +76,50 @@ __device__ __forceinline__ int wave_max_i(int x) {
 
 struct WorkItem {
   int b, g, head0, row_blk;
+  int unit;   // (b, g, head slice) index
+  int piece;  // piece of the split plan, -1 without one
 };
 
 __device__ __forceinline__ bool decode_item(const FwdParams& p, WorkItem& w) {
   int bid = blockIdx.x;
   int xcd = bid % kNumXcd;
   int slot = bid / kNumXcd;
-  int W = xcd * p.per_xcd + slot;
-  if (W >= p.n_items) return false;
-  int hs = W % p.nhs;
-  int t = W / p.nhs;
-  int rb_desc = t % p.nrb;
-  t /= p.nrb;
-  w.g = t % p.Hkv;
-  w.b = t / p.Hkv;
-  w.row_blk = p.nrb - 1 - rb_desc;  // heavy first: later rows hold later positions
+  int hs, k, bg;
+  if (p.n_pieces) {
+    // split plan: each XCD owns per_xcd (batch, kv head) pairs and runs their pieces heaviest
+    // first across all of them (piece index outermost)
+    hs = slot % p.nhs;
+    int t = slot / p.nhs;
+    const int pl = t % p.per_xcd;
+    k = t / p.per_xcd;
+    bg = xcd * p.per_xcd + pl;
+    if (k >= p.n_pieces || bg >= p.B * p.Hkv) return false;
+    w.piece = k;  // pieces are listed heaviest first
+    w.row_blk = p.piece_rb[k];
+  } else {
+    int W = xcd * p.per_xcd + slot;
+    if (W >= p.n_items) return false;
+    hs = W % p.nhs;
+    int t = W / p.nhs;
+    k = t % p.nrb;
+    bg = t / p.nrb;
+    w.piece = -1;
+    w.row_blk = p.nrb - 1 - k;  // heavy first: later rows hold later positions
+  }
+  w.g = bg % p.Hkv;
+  w.b = bg / p.Hkv;
+  w.unit = bg * p.nhs + hs;
   w.head0 = w.g * p.G + hs * p.hpw;
   return true;
+}
+
+// Key tiles a row block visits (chunks 0..imax in original order, BK-key tiles, the last chunk
+// cut at the block's largest position qmax): the same count on the host and the device.
+__host__ __device__ inline int visible_tiles(int qmax, int c, int cp, int bk) {
+  const int imax = qmax / c < 2 * cp - 1 ? qmax / c : 2 * cp - 1;
+  const int tpc = (c + bk - 1) / bk;
+  const int in_last = (qmax - imax * c + 1 + bk - 1) / bk;
+  return imax * tpc + (in_last < tpc ? in_last : tpc);
 }
 
 // Shared prologue: the row positions of this lane and the workgroup's [qmin, qmax].
@@ -163,6 +205,10 @@ inline FwdParams make_params(const AttnArgs& a) {
   p.n_items = p.B * p.Hkv * p.nrb * p.nhs;
   p.per_xcd = (p.n_items + kNumXcd - 1) / kNumXcd;
   p.scale_log2 = a.scale * kLog2e;
+  p.n_pieces = 0;
+  p.n_slots = 0;
+  p.part_o = nullptr;
+  p.part_ml = nullptr;
   return p;
 }
 

@@ -86,7 +86,11 @@ struct AttnArgs {
   float* lse;            // may be null
   int batch, seq, sq, hq, hkv, d_qk, d_v, cp, rank;
   float scale;
+  void* ws = nullptr;     // optional workspace for the split of heavy row blocks (bf16)
+  size_t ws_bytes = 0;
 };
+// Workspace the bf16 forward uses to split heavy row blocks (0: no split for this shape).
+size_t attn_fwd_workspace_bytes(const AttnArgs& a);
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream);
 

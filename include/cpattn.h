@@ -127,6 +127,33 @@ int cp_attention_fwd(const void* q_shard, const void* k, const void* v,
                      int32_t d_qk, int32_t d_v, int32_t dtype, float softmax_scale,
                      int32_t cp, int32_t rank, void* stream);
 
+/* cp_attention_fwd_ws: cp_attention_fwd with an optional caller workspace, which lets the bf16
+ * forward balance small grids in time as well as in work. "Add context parallelism" (PR 1445,
+ * Description) balances the ranks so that they take a similar amount of work and hence time;
+ * inside one rank, a grid with fewer than two 256-row work items per compute unit (the 8192-token
+ * shape at cp = 4) is otherwise timed by its heaviest row block. With the workspace, the visible
+ * key tiles of heavy row blocks are cut into pieces computed by separate workgroups, each writing
+ * an unnormalised output with its running maximum and row sum, and a second kernel merges them
+ * (O = sum_i w_i o_i / sum_i w_i l_i, w_i = exp(m_i - max m)). Same arguments, results and
+ * errors as cp_attention_fwd, plus:
+ *   workspace, workspace_bytes: device scratch of at least cp_attention_fwd_workspace_bytes(...)
+ *            bytes, owned by the caller, 16-byte aligned; contents on entry do not matter; calls
+ *            sharing one workspace must not overlap. NULL, a smaller workspace, explicit
+ *            q_positions or float32 inputs run exactly as cp_attention_fwd (no split).
+ * cp_attention_fwd_workspace_bytes: the bytes the split needs for the rank's own shard of this
+ * shape (q_positions == NULL, sq = seq / cp); 0 when this shape is not split (grids with enough
+ * work items, float32) or the arguments are invalid. */
+size_t cp_attention_fwd_workspace_bytes(int32_t batch, int32_t seq, int32_t hq, int32_t hkv,
+                                        int32_t d_qk, int32_t d_v, int32_t dtype, int32_t cp,
+                                        int32_t rank);
+
+int cp_attention_fwd_ws(const void* q_shard, const void* k, const void* v,
+                        const int32_t* q_positions, void* o, float* lse,
+                        int32_t batch, int32_t seq, int32_t sq, int32_t hq, int32_t hkv,
+                        int32_t d_qk, int32_t d_v, int32_t dtype, float softmax_scale,
+                        int32_t cp, int32_t rank, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Backward pass of cp_attention_fwd for one rank ("Add context parallelism", PR 1445,
  * Description: context parallelism serves training on long sequences, so each rank also

@@ -36,6 +36,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("cp_load_balance_permute", "cp_load_balance_unpermute", "cp_attention_fwd",
+                 "cp_attention_fwd_ws", "cp_attention_fwd_workspace_bytes", "gqa_decode_attention_noalloc",
                  "gqa_decode_attention", "gqa_decode_workspace_bytes", "cpattn_last_error",
                  "cp_load_balance_source_index", "cp_load_balance_positions", "gqa_decode_merge",
                  "gqa_decode_attention_int8kv", "kv_cache_quantize_int8", "cp_attention_bwd",
@@ -124,6 +125,31 @@ def _fwd(lib, **kw):
 def test_attention_argument_errors(lib, kw, status, substr):
     rc, msg = _fwd(lib, **kw)
     assert rc == status and substr in msg, (rc, msg)
+
+
+def test_attention_fwd_workspace_bytes(lib):
+    # the 8192-token MHA shape at cp = 4 (256 work items) is split; the 131072-token GQA and the
+    # 32768-token MLA shapes (4096 work items per rank) and float32 are not; bad arguments give 0
+    bf16, f32 = binding.CPA_BF16, binding.CPA_F32
+    assert all(lib.cp_attention_fwd_workspace_bytes(1, 8192, 32, 32, 128, 128, bf16, 4, r) > 0 for r in range(4))
+    assert lib.cp_attention_fwd_workspace_bytes(1, 8192, 32, 32, 128, 128, bf16, 1, 0) == 0
+    assert lib.cp_attention_fwd_workspace_bytes(1, 131072, 64, 8, 128, 128, bf16, 8, 3) == 0
+    assert lib.cp_attention_fwd_workspace_bytes(1, 32768, 128, 128, 192, 128, bf16, 4, 0) == 0
+    assert lib.cp_attention_fwd_workspace_bytes(1, 2048, 1, 1, 128, 128, f32, 1, 0) == 0
+    assert lib.cp_attention_fwd_workspace_bytes(1, 2047, 1, 1, 128, 128, bf16, 1, 0) == 0
+    assert lib.cp_attention_fwd_workspace_bytes(1, 2048, 1, 1, 96, 96, bf16, 1, 0) == 0
+    assert lib.cp_attention_fwd_workspace_bytes(1, 2048, 1, 1, 128, 128, bf16, 2, 2) == 0
+
+
+def test_attention_fwd_ws_argument_errors(lib):
+    rc = lib.cp_attention_fwd_ws(FAKE, FAKE, FAKE, None, FAKE, None, 1, 8192, 2048, 32, 32, 128, 128,
+                                 binding.CPA_BF16, 0.088, 4, 0, ctypes.c_void_p(4100), 1 << 30, None)
+    rc, msg = _status_and_message(lib, rc)
+    assert rc == binding.CPA_EINVAL and "workspace" in msg, (rc, msg)
+    rc = lib.cp_attention_fwd_ws(FAKE, FAKE, FAKE, None, FAKE, None, 1, 8192, 2048, 32, 32, 128, 128,
+                                 binding.CPA_BF16, 0.088, 4, 4, FAKE, 1 << 30, None)
+    rc, msg = _status_and_message(lib, rc)
+    assert rc == binding.CPA_EINVAL and "rank" in msg, (rc, msg)
 
 
 def test_attention_empty_is_ok_without_device(lib):

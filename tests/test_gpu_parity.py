@@ -99,6 +99,40 @@ def test_attention_small_all_ranks(case):
             check_rank(pf, cp, r, tag=name)
 
 
+SPLIT_CASES = [
+    # name, batch, seq, cp, hq, hkv, dqk, dv, seed: shapes whose grids are small enough for the
+    # forward to cut heavy row blocks' key ranges into pieces (a workspace is passed)
+    ("split-mha-cp1", 1, 2048, 1, 1, 1, 128, 128, 61),
+    ("split-gqa-g8", 1, 2048, 2, 16, 2, 128, 128, 62),
+    ("split-mla-192", 1, 1024, 2, 2, 2, 192, 128, 63),
+    ("split-d64-g4", 1, 2048, 2, 4, 1, 64, 64, 64),
+    ("split-ragged-b2", 2, 2400, 3, 2, 2, 128, 128, 65),   # c = 400: row blocks straddle both chunks
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_attention_split_heavy_row_blocks(case):
+    """The key-range split of heavy row blocks (cp_attention_fwd_ws): every row of every rank
+    against the oracle, and against the unsplit call on the same inputs."""
+    name, batch, seq, cp, hq, hkv, dqk, dv, seed = case
+    pf = Prefill(batch, seq, hq, hkv, dqk, dv, torch.bfloat16, seed)
+    kp, vp = pf.kv_perm(cp)
+    c = seq // (2 * cp)
+    for r in range(cp):
+        need = cpa.attention_fwd_workspace_bytes(batch, seq, hq, hkv, dqk, dv, torch.bfloat16, cp, r)
+        announce(f"{name} rank {r}: split workspace {need} bytes")
+        assert need > 0, "this shape was chosen to be split"
+        ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)  # garbage: contents must not matter
+        qs = cpa.permute(pf.qd, cp, row_begin=r * 2 * c, row_count=2 * c)
+        o, lse = cpa.attention_fwd(qs, kp, vp, cp, r, scale=pf.scale, workspace=ws)
+        o1, lse1 = cpa.attention_fwd(qs, kp, vp, cp, r, scale=pf.scale, split=False)
+        torch.cuda.synchronize()
+        O_ref, L_ref = pf.oracle_rank(cp, r)
+        assert_close(o.float().cpu().numpy(), O_ref, 2e-2, f"{name} split O r{r}")
+        assert_close(lse.cpu().numpy(), L_ref, 2e-2, f"{name} split LSE r{r}")
+        assert_close(o.float().cpu().numpy(), o1.float().cpu().numpy(), 2e-2, f"{name} split vs unsplit O r{r}")
+
+
 def test_sharded_outputs_reassemble_to_full_causal_attention():
     """Concatenated, un-permuted per-rank outputs equal un-sharded causal attention (the
     relation the CP unit test of PR 2023 checks), on the GPU and against the oracle."""

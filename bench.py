@@ -20,7 +20,8 @@ lengths uniform in [1024, 2048]), rotating 4 cache copies so reads come from HBM
 the 256 MB last-level cache; the same decode over an int8-quantized cache (6 copies); every
 rank's attention kernel at the other prefill shapes (`other_configs`: Llama2-7B MHA at 8192
 tokens, cp 1 and 4; DeepSeek-V3 MLA at 32768 tokens, cp 4; skip with --no-other-configs); and
-the CPU fp64 oracle on a bounded row sample of the same prefill workload (the CPU baseline).
+the CPU fp64 oracle on a bounded row sample of the same prefill workload (the CPU baseline),
+plus the oracle over whole workloads at the small configs (`cpu_baseline.full_configs`).
 
 Prints one JSON line.
 """
@@ -395,6 +396,42 @@ def cpu_baseline(w, cp, rank, n_rows, seed=0):
                 seconds=dt)
 
 
+def cpu_baseline_full_configs():
+    """Time the CPU fp64 oracle (as it is) over whole workloads at the small configs: every rank
+    of the 512-token cp=2 fp32 case, the 8192-token Llama2-7B shape at cp=1 and every rank at
+    cp=4 (each rank's permutes of its windows plus attention over its full shard), and the
+    Mixtral-8x22B-shaped decode over the whole batch. Rates are useful causal TFLOP/s for the
+    prefills and algorithmic GB/s for the decode."""
+    from context_causal_attention_load_amd import synth
+    from oracle import attention as oatt
+    from oracle import lb_index as olb
+
+    out = []
+    for w in (synth.TINY_CP2_F32, synth.LLAMA2_7B_S8K):
+        q, k, v = synth.workload_prefill_inputs(w)
+        for cp in w.cps:
+            S, c = w.seq, w.seq // (2 * cp)
+            t0 = time.perf_counter()
+            for r in range(cp):
+                qs = oatt.permute_ref(q, S, cp, r * 2 * c, 2 * c)
+                kp = oatt.permute_ref(k, S, cp)
+                vp = oatt.permute_ref(v, S, cp)
+                oatt.cp_attention_ref(qs, kp, vp, olb.shard_positions(S, cp, r), S, cp, w.scale)
+            dt = time.perf_counter() - t0
+            flops = cp * useful_flops(S, cp, w.hq, w.d_qk, w.d_v, w.batch)
+            out.append({"workload": f"{w.name} cp={cp}, all {cp} rank(s)", "seconds": round(dt, 3),
+                        "value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s"})
+    dw = synth.MIXTRAL_8X22B_DECODE
+    lengths, q, kc, vc = synth.workload_decode_inputs(dw)
+    t0 = time.perf_counter()
+    oatt.decode_ref(q, kc, vc, lengths.numpy(), dw.scale)
+    dt = time.perf_counter() - t0
+    nbytes = decode_bytes(dw, lengths)
+    out.append({"workload": dw.name, "seconds": round(dt, 3), "value": round(nbytes / dt / 1e9, 3),
+                "unit": "GB/s"})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -505,6 +542,7 @@ def main():
         cb = cpu_baseline(w, cp, 0, args.cpu_rows)
         cb.pop("seconds")
         result["cpu_baseline"] = {k: (round(v, 5) if isinstance(v, float) else v) for k, v in cb.items()}
+        result["cpu_baseline"]["full_configs"] = cpu_baseline_full_configs()
     print(json.dumps(result), flush=True)
 
 

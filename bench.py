@@ -21,7 +21,9 @@ the 256 MB last-level cache; the same decode over an int8-quantized cache (6 cop
 rank's attention kernel at the other prefill shapes (`other_configs`: Llama2-7B MHA at 8192
 tokens, cp 1 and 4; DeepSeek-V3 MLA at 32768 tokens, cp 4; skip with --no-other-configs); and
 the CPU fp64 oracle on a bounded row sample of the same prefill workload (the CPU baseline),
-plus the oracle over whole workloads at the small configs (`cpu_baseline.full_configs`).
+plus the oracle over whole workloads at the small configs (`cpu_baseline.full_configs`). A plain
+bf16 GEMM through torch.matmul is timed last as a reference for the matrix-core rate the part
+sustains (`gemm_reference`; skip with --no-gemm-reference).
 
 Prints one JSON line.
 """
@@ -248,6 +250,29 @@ def _time_calls(call, iters):
     return ms, t0.elapsed_time(t1) / iters
 
 
+def gemm_reference(dev, n=16384, iters=10):
+    """Sustained rate of a plain bf16 GEMM (n x n x n through torch.matmul, i.e. the vendor BLAS)
+    on this part in the same run: a reference for how much of the spec-sheet matrix-core peak the
+    part holds under load, so the attention kernel's fraction of peak can be read against it. Not
+    part of the attention path."""
+    a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del a, b, c
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"shape": f"{n}x{n}x{n} bf16 torch.matmul", "ms": round(ms, 3), "tflops": round(tf, 1),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def other_configs_ms(dev, iters=5):
     """Every rank's attention kernel at the other prefill shapes (the 8192-token Llama2-7B MHA at
     cp = 1 and cp = 4, the 32768-token DeepSeek-V3 MLA shape at cp = 4): HIP-event time of one
@@ -447,6 +472,8 @@ def main():
                     help="skip the per-rank balanced vs contiguous shard timing (after the timed steps)")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the per-rank attention timing at the other prefill shapes")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the plain bf16 GEMM timed as a reference for the part's sustained matrix-core rate")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share (one context-parallel rank) and does not run on more than "
@@ -538,6 +565,8 @@ def main():
                          "traffic_unit": "HBM bytes per call (split + merge)", "algorithmic_bytes": d8["bytes"]}}
     if not args.no_other_configs:
         result["other_configs"] = other_configs_ms(dev)
+    if not args.no_gemm_reference:
+        result["gemm_reference"] = gemm_reference(dev)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, cp, 0, args.cpu_rows)
         cb.pop("seconds")

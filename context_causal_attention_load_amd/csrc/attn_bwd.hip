@@ -172,22 +172,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
   const int c = p.c;
   const int imax = min(qmax / c, 2 * p.cp - 1);
 
+  // DMA slots: wave-instruction (u, wave) fills LDS bytes [1024 (u kWaves + wave), + 1024) of a
+  // tile, lane l at + 16 l, from whichever (row, chunk) the swizzle puts there. The per-lane rows
+  // and columns are kept in registers, except at Dqk > 128, where they are recomputed for every
+  // tile from an opaque copy of the lane index (the registers are needed elsewhere).
   constexpr int K_DMA = C::K_LOADS, V_DMA = C::V_LOADS;
+  constexpr bool kKeepDmaGeometry = DQK <= 128;
+  auto dma_geometry = [](int u, int wv, int ln, int ch, int& row, unsigned& col) {
+    const int pos = (u * kWaves + wv) * 1024 + ln * 16;
+    row = pos / (ch * 16);
+    const int phys = (pos % (ch * 16)) / 16;
+    col = (unsigned)((phys ^ (ch == C::KCH ? swz<C::KCH>(row) : swz<C::VCH>(row))) * 16);
+  };
   int k_row[K_DMA], v_row[V_DMA];
   unsigned k_col[K_DMA], v_col[V_DMA];
+  if constexpr (kKeepDmaGeometry) {
 #pragma unroll
-  for (int u = 0; u < K_DMA; ++u) {
-    const int pos = (u * kWaves + wave) * 1024 + lane * 16;
-    const int row = pos / (C::KCH * 16), phys = (pos % (C::KCH * 16)) / 16;
-    k_row[u] = row;
-    k_col[u] = (unsigned)((phys ^ swz<C::KCH>(row)) * 16);
-  }
+    for (int u = 0; u < K_DMA; ++u) dma_geometry(u, wave, lane, C::KCH, k_row[u], k_col[u]);
 #pragma unroll
-  for (int u = 0; u < V_DMA; ++u) {
-    const int pos = (u * kWaves + wave) * 1024 + lane * 16;
-    const int row = pos / (C::VCH * 16), phys = (pos % (C::VCH * 16)) / 16;
-    v_row[u] = row;
-    v_col[u] = (unsigned)((phys ^ swz<C::VCH>(row)) * 16);
+    for (int u = 0; u < V_DMA; ++u) dma_geometry(u, wave, lane, C::VCH, v_row[u], v_col[u]);
   }
   const unsigned lds0 = (unsigned)(uintptr_t)lds;
   auto dma_tile = [&](const TileCursor& tc, int b) {
@@ -197,23 +200,48 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
     const char* vt = vbase + prow0 * kv_row_bytes_v;
     const unsigned kl = lds0 + b * C::STAGE;
     const unsigned vl = kl + C::K_BYTES;
+    int ln = lane;
+    if constexpr (!kKeepDmaGeometry) asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int u = 0; u < K_DMA; ++u)
-      dma16_sv(kt, (unsigned)(min(k_row[u], last) * kv_row_bytes_k) + k_col[u], kl + (u * kWaves + wave) * 1024);
+    for (int u = 0; u < K_DMA; ++u) {
+      int row = 0;
+      unsigned col = 0;
+      if constexpr (kKeepDmaGeometry) {
+        row = k_row[u];
+        col = k_col[u];
+      } else {
+        dma_geometry(u, wave, ln, C::KCH, row, col);
+      }
+      dma16_sv(kt, (unsigned)(min(row, last) * kv_row_bytes_k) + col, kl + (u * kWaves + wave) * 1024);
+    }
 #pragma unroll
-    for (int u = 0; u < V_DMA; ++u)
-      dma16_sv(vt, (unsigned)(min(v_row[u], last) * kv_row_bytes_v) + v_col[u], vl + (u * kWaves + wave) * 1024);
+    for (int u = 0; u < V_DMA; ++u) {
+      int row = 0;
+      unsigned col = 0;
+      if constexpr (kKeepDmaGeometry) {
+        row = v_row[u];
+        col = v_col[u];
+      } else {
+        dma_geometry(u, wave, ln, C::VCH, row, col);
+      }
+      dma16_sv(vt, (unsigned)(min(row, last) * kv_row_bytes_v) + col, vl + (u * kWaves + wave) * 1024);
+    }
   };
 
   f32x16 dqacc[C::MQ];
 #pragma unroll
   for (int m = 0; m < C::MQ; ++m) dqacc[m] = f32x16{};
-  // the MFMA seeds as full vectors (32 registers, read in place by the products)
+  // The MFMA seeds as full vectors, read in place by the products (32 registers). At Dqk > 128
+  // the Q fragments and dQ accumulators leave no room for them: the seeds are then written
+  // into the accumulators from the two scalars for each 32-key block instead.
+  constexpr bool kSeedVectors = DQK <= 128;
   f32x16 seed_l, seed_d;
+  if constexpr (kSeedVectors) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    seed_l[r] = neg_l2;
-    seed_d[r] = neg_d;
+    for (int r = 0; r < 16; ++r) {
+      seed_l[r] = neg_l2;
+      seed_d[r] = neg_d;
+    }
   }
 
   TileCursor tc{0, 0};
@@ -248,7 +276,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
       const int krow = mb * 32 + (ln & 31);
-      f32x16 sacc = seed_l, dacc = seed_d;
+      f32x16 sacc, dacc;
+      if constexpr (kSeedVectors) {
+        sacc = seed_l;
+        dacc = seed_d;
+      } else {
+        // opaque copies, so the fills are not hoisted out of the loop as full vectors again
+        float nl = neg_l2, nd = neg_d;
+        asm volatile("" : "+v"(nl), "+v"(nd));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[r] = nl;
+          dacc[r] = nd;
+        }
+      }
       const char* kr = kb + krow * (C::KCH * 16);
       const int swk = swz<C::KCH>(krow);
 #pragma unroll

@@ -273,11 +273,12 @@ def gemm_reference(dev, n=16384, iters=10):
             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
-def other_configs_ms(dev, iters=5):
+def other_configs_ms(dev, iters=5, bwd_iters=3):
     """Every rank's attention kernel at the other prefill shapes (the 8192-token Llama2-7B MHA at
     cp = 1 and cp = 4, the 32768-token DeepSeek-V3 MLA shape at cp = 4): HIP-event time of one
-    launch after a warm-up, median of ``iters``. Inputs are seeded N(0,1) draws on the device
-    (timing only; these shapes' parity is in the tests)."""
+    launch after a warm-up, median of ``iters``; then every rank's backward call, median of
+    ``bwd_iters``. Inputs are seeded N(0,1) draws on the device (timing only; these shapes'
+    parity is in the tests)."""
     import context_causal_attention_load_amd as cpa
     from context_causal_attention_load_amd import synth
 
@@ -295,7 +296,13 @@ def other_configs_ms(dev, iters=5):
             need = max(cpa.attention_fwd_workspace_bytes(w.batch, w.seq, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype, cp, r)
                        for r in range(cp))
             ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-            ms = []
+            d_o = torch.randn((w.batch, 2 * c, w.hq, w.d_v), generator=gen, device=dev,
+                              dtype=torch.float32).to(w.dtype)
+            dq = torch.empty((w.batch, 2 * c, w.hq, w.d_qk), dtype=torch.float32, device=dev)
+            dk = torch.empty((w.batch, w.seq, w.hkv, w.d_qk), dtype=torch.float32, device=dev)
+            dv = torch.empty((w.batch, w.seq, w.hkv, w.d_v), dtype=torch.float32, device=dev)
+            bws = torch.empty(cpa.attention_bwd_workspace_bytes(w.batch, 2 * c, w.hq), dtype=torch.uint8, device=dev)
+            ms, bms = [], []
             for r in range(cp):
                 qs = cpa.permute(qd, cp, row_begin=r * 2 * c, row_count=2 * c)
                 cpa.attention_fwd(qs, kp, vp, cp, r, scale=w.scale, out=o, lse=lse, workspace=ws)
@@ -306,13 +313,31 @@ def other_configs_ms(dev, iters=5):
                     b.record()
                 torch.cuda.synchronize()
                 ms.append(sorted(a.elapsed_time(b) for a, b in evs)[iters // 2])
+                def bwd(qs=qs, r=r):
+                    cpa.attention_bwd(qs, kp, vp, o, lse, d_o, cp, r, scale=w.scale, workspace=bws, dq=dq, dk=dk, dv=dv)
+
+                bwd()
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(bwd_iters)]
+                for a, b in evs:
+                    a.record()
+                    bwd()
+                    b.record()
+                torch.cuda.synchronize()
+                bms.append(sorted(a.elapsed_time(b) for a, b in evs)[bwd_iters // 2])
             flops = useful_flops(w.seq, cp, w.hq, w.d_qk, w.d_v, w.batch)
             avg = sum(ms) / len(ms)
             tf = flops / (avg * 1e-3) / 1e12
+            bflops = backward_flops(w.seq, cp, w.hq, w.d_qk, w.d_v, w.batch)
+            bavg = sum(bms) / len(bms)
+            btf = bflops / (bavg * 1e-3) / 1e12
             out.append({"workload": f"{w.name} cp={cp}", "ms_per_rank": [round(x, 3) for x in ms],
                         "rank_max_over_mean": round(max(ms) / avg, 4), "heavy_row_blocks_split": need > 0,
                         "useful_flop_per_rank": flops, "tflops": round(tf, 1),
-                        "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+                        "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "backward": {"ms_per_rank": [round(x, 3) for x in bms], "useful_flop_per_rank": bflops,
+                                     "tflops": round(btf, 1), "frac_of_bf16_peak": round(btf / PEAK_BF16_TFLOPS, 4)}})
+            del d_o, dq, dk, dv, bws
         del qd, kd, vd
     return out
 

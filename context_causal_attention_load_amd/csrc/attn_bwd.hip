@@ -391,6 +391,10 @@ struct DkvCfg {
   static constexpr int DV_STEPS = DV / 16;
   static constexpr int MK = DQK / 32;
   static constexpr int MV = DV / 32;
+  // Dqk > 128: one wave per SIMD, so nothing covers a wave's own waits. It then takes two stages
+  // per barrier (see the pair loop), through a ring of three pairs.
+  static constexpr bool PAIR = DQK > 128;
+  static constexpr int RING = PAIR ? 6 : kKvStages;
 };
 
 struct DkvParams {
@@ -410,11 +414,152 @@ __device__ __forceinline__ int load_uniform_i32(const int* ptr) {
   return v;
 }
 
+// One dkdv stage in three steps (the pair loop orders them across two stages).
+// Step 1: S = Q K'^T - LSE and dP - D = dO V^T - D for the stage in LDS at qt (its Q tile, then
+// its dO tile, then log2-LSE, D and positions of its 32 rows).
+// With SCHED, S and dP k-steps alternate and each row-fragment read is kept two MFMAs ahead of
+// its use (the single-stage loop); without, the compiler orders both stages of a pair.
+template <int DQK, int DV, bool SCHED>
+__device__ __forceinline__ void dkdv_scores(const char* qt, const bf16x8 (&kf)[DQK / 16], const bf16x8 (&vf)[DV / 16],
+                                            f32x16& sacc, f32x16& dacc) {
+  using C = DkvCfg<DQK, DV>;
+  int ln = threadIdx.x % 64;
+  asm volatile("" : "+v"(ln));
+  const int row = ln & 31, lhl = ln >> 5;
+  const char* ot = qt + C::Q_BYTES;
+  const float* st_lse = reinterpret_cast<const float*>(ot + C::O_BYTES);
+  const float* st_dlt = st_lse + kBQ;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(st_lse + 8 * i + 4 * lhl);
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(st_dlt + 8 * i + 4 * lhl);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sacc[4 * i + j] = -l4[j];
+      dacc[4 * i + j] = -d4[j];
+    }
+  }
+  const char* qr = qt + row * (C::QCH * 16);
+  const char* orow = ot + row * (C::OCH * 16);
+  // chunk (2 ks + hl) ^ sw = 2 ks ^ (hl ^ sw): one xor per k-step on a per-lane constant
+  const unsigned tq = (unsigned)(lhl ^ swz<C::QCH>(row)), to = (unsigned)(lhl ^ swz<C::OCH>(row));
+  if constexpr (SCHED) {
+#pragma unroll
+    for (int ks = 0; ks < (C::QK_STEPS > C::DV_STEPS ? C::QK_STEPS : C::DV_STEPS); ++ks) {
+      if (ks < C::QK_STEPS) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + ((tq ^ (2u * ks)) << 4));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
+      }
+      if (ks < C::DV_STEPS) {
+        // with equal row layouts the dO tile's offsets are the Q tile's plus its size
+        const bf16x8 a = C::QCH == C::OCH ? *reinterpret_cast<const bf16x8*>(qr + ((tq ^ (2u * ks)) << 4) + C::Q_BYTES)
+                                          : *reinterpret_cast<const bf16x8*>(orow + ((to ^ (2u * ks)) << 4));
+        dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dacc, 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < C::QK_STEPS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + ((tq ^ (2u * ks)) << 4));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::DV_STEPS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + ((to ^ (2u * ks)) << 4));
+      dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dacc, 0, 0, 0);
+    }
+  }
+  if constexpr (SCHED) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < C::QK_STEPS + C::DV_STEPS - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+}
+
+// Step 2: mask (when the stage's rows do not all see every key of the workgroup, or keys run
+// past the valid ones), then P and dS in bf16 in the B-operand layout of step 3.
+template <int DQK, int DV>
+__device__ __forceinline__ void dkdv_probs(const char* qt, bool need_mask, int kk, int kpos, int nvalid, f32x16 sacc,
+                                           const f32x16& dacc, bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
+  using C = DkvCfg<DQK, DV>;
+  if (need_mask) {
+    const int lhl = (threadIdx.x % 64) >> 5;
+    const int* st_pos = reinterpret_cast<const int*>(qt + C::Q_BYTES + C::O_BYTES + 2 * kBQ * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int4 q4 = *reinterpret_cast<const int4*>(st_pos + 8 * i + 4 * lhl);
+      const int qp[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sacc[4 * i + j] = (kk < nvalid && kpos <= qp[j]) ? sacc[4 * i + j] : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float pr = __builtin_amdgcn_exp2f(sacc[r]);
+    pb[r / 8][r % 8] = (__bf16)pr;
+    dsb[r / 8][r % 8] = (__bf16)(pr * dacc[r]);
+  }
+}
+
+// Step 3: dV^T += dO^T P and dK^T += Q^T dS, A operands from transposing reads of the tiles.
+template <int DQK, int DV, bool SCHED>
+__device__ __forceinline__ void dkdv_grads(const char* qt, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2],
+                                           f32x16 (&dkacc)[DQK / 32], f32x16 (&dvacc)[DV / 32]) {
+  using C = DkvCfg<DQK, DV>;
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  int ln = threadIdx.x % 64;
+  asm volatile("" : "+v"(ln));
+  const int lgrp = ln >> 4, ltr_e = (ln & 15) >> 2, ltr_q = ln & 3;
+  const char* ot = qt + C::Q_BYTES;
+  const unsigned cbase = 16u * (unsigned)(lgrp & 1) + 4u * (unsigned)ltr_q;
+  const int row_a0 = 4 * (lgrp >> 1) + ltr_e, row_b0 = row_a0 + 8;
+  const unsigned c0 = cbase >> 3, within = (cbase & 7u) * 2u;
+  const unsigned ta = c0 ^ (unsigned)swz<C::OCH>(row_a0), tb = c0 ^ (unsigned)swz<C::OCH>(row_b0);
+  const unsigned qa = c0 ^ (unsigned)swz<C::QCH>(row_a0), qb = c0 ^ (unsigned)swz<C::QCH>(row_b0);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int row_a = 16 * ks + row_a0;
+    const int row_b = row_a + 8;
+#pragma unroll
+    for (int m = 0; m < C::MV; ++m) {
+      const char* pa = ot + row_a * (C::OCH * 16) + ((ta ^ (4u * m)) << 4) + within;
+      const char* pb2 = ot + row_b * (C::OCH * 16) + ((tb ^ (4u * m)) << 4) + within;
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
+      i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[ks], dvacc[m], 0, 0, 0);
+    }
+#pragma unroll
+    for (int m = 0; m < C::MK; ++m) {
+      const char* pa = qt + row_a * (C::QCH * 16) + ((qa ^ (4u * m)) << 4) + within;
+      const char* pb2 = qt + row_b * (C::QCH * 16) + ((qb ^ (4u * m)) << 4) + within;
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
+      i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), dsb[ks], dkacc[m], 0, 0, 0);
+    }
+  }
+  if constexpr (SCHED) {
+    // keep the transposing reads (two per MFMA) ahead of their MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * (C::MV + C::MK) - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+}
+
 template <int DQK, int DV>
 __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU) void attn_bwd_dkdv_kernel(
     DkvParams p, BwdExtra e) {
   using C = DkvCfg<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) char lds[kKvStages * C::STAGE];
+  __shared__ __attribute__((aligned(16))) char lds[C::RING * C::STAGE];
 
   // work item: (b, g, chunk i, tile t). Each XCD takes a contiguous range of items, in which
   // tiles and chunks vary fastest, so an XCD holds whole kv heads (equal work) and its L2 serves
@@ -526,9 +671,6 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA) : "memory");
   };
 
-  const int grp = lane / 16;
-  const int tr_e = (lane % 16) / 4;
-  const int tr_q = lane % 4;
   const int kpos = kpos0 + kk;
 
   // stage sequence: (query block, head of the group), heads fastest; qb < 0 marks the end
@@ -539,6 +681,92 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
       sqb = prev_visible(sqb - 1);
     }
   };
+  if constexpr (C::PAIR) {
+    // Two stages per barrier: the pair (A, B) is in LDS while the next pair's copies land and
+    // the one after is issued into the slots of the previous pair (six slots, three pairs).
+    // Within the pair the steps run as S(A); probs(A) with S(B); grads(A) with probs(B);
+    // grads(B), so that one stage's softmax overlaps the other stage's matrix products.
+    int sq[4], sh[4];  // stages A, B (in LDS) and C, D (in flight); qb < 0: none
+    sq[0] = prev_visible(e.nqb - 1);
+    sh[0] = 0;
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      sq[i] = sq[i - 1];
+      sh[i] = sh[i - 1];
+      advance(sq[i], sh[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (sq[i] >= 0) dma_stage(sq[i], g * p.G + sh[i], i);
+    // A and B must have landed; C and D may stay in flight
+    if (sq[3] >= 0) {
+      if (wave < 3)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (C::Q_DMA + C::O_DMA + 1)) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (C::Q_DMA + C::O_DMA)) : "memory");
+    } else if (sq[2] >= 0) {
+      if (wave < 3)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA + 1) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    int slot = 0;  // ring slot of A; B is slot + 1
+    while (sq[0] >= 0) {
+      int eq = sq[3], eh = sh[3];
+      advance(eq, eh);
+      int fq = eq, fh = eh;
+      advance(fq, fh);
+      const int se = slot + 4 >= C::RING ? slot + 4 - C::RING : slot + 4;  // the previous pair's slots
+      if (eq >= 0) dma_stage(eq, g * p.G + eh, se);
+      if (fq >= 0) dma_stage(fq, g * p.G + fh, se + 1);
+
+      const char* qa = lds + slot * C::STAGE;
+      const char* qb_t = qa + C::STAGE;
+      const bool has_b = sq[1] >= 0;
+      const bool mask_a = load_uniform_i32(blkmin + sq[0]) < kpos0 + C::BKV - 1 || nvalid < C::BKV ||
+                          (sq[0] + 1) * kBQ > p.Sq;
+      const bool mask_b = has_b && (load_uniform_i32(blkmin + sq[1]) < kpos0 + C::BKV - 1 || nvalid < C::BKV ||
+                                    (sq[1] + 1) * kBQ > p.Sq);
+      f32x16 sa, da, sb, db;
+      bf16x8 pba[2], dsa[2], pbb[2], dsbb[2];
+      dkdv_scores<DQK, DV, false>(qa, kf, vf, sa, da);
+      dkdv_probs<DQK, DV>(qa, mask_a, kk, kpos, nvalid, sa, da, pba, dsa);
+      if (has_b) dkdv_scores<DQK, DV, false>(qb_t, kf, vf, sb, db);
+      dkdv_grads<DQK, DV, false>(qa, pba, dsa, dkacc, dvacc);
+      if (has_b) {
+        dkdv_probs<DQK, DV>(qb_t, mask_b, kk, kpos, nvalid, sb, db, pbb, dsbb);
+        dkdv_grads<DQK, DV, false>(qb_t, pbb, dsbb, dkacc, dvacc);
+      }
+
+      // the next pair's copies must have landed; the pair after may stay in flight
+      if (fq >= 0) {
+        if (wave < 3)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (C::Q_DMA + C::O_DMA + 1)) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (C::Q_DMA + C::O_DMA)) : "memory");
+      } else if (eq >= 0) {
+        if (wave < 3)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA + 1) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();
+      slot = slot + 2 >= C::RING ? slot + 2 - C::RING : slot + 2;
+      sq[0] = sq[2];
+      sh[0] = sh[2];
+      sq[1] = sq[3];
+      sh[1] = sh[3];
+      sq[2] = eq;
+      sh[2] = eh;
+      sq[3] = fq;
+      sh[3] = fh;
+    }
+  } else {
   int qb = prev_visible(e.nqb - 1), h = 0;
   int qb1 = qb, h1 = h;
   advance(qb1, h1);
@@ -558,125 +786,17 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
     if (qb2 >= 0) dma_stage(qb2, g * p.G + h2, buf2);  // that slot was last read two stages ago
 
     const char* qt = lds + buf * C::STAGE;
-    const char* ot = qt + C::Q_BYTES;
-    const float* st_lse = reinterpret_cast<const float*>(ot + C::O_BYTES);
-    const float* st_dlt = st_lse + kBQ;
-    const int* st_pos = reinterpret_cast<const int*>(st_dlt + kBQ);
 
-    // Lane-dependent LDS offsets are recomputed from an opaque copy of the lane index in every
-    // stage: hoisted out of the loop they would hold ~40 registers and push the kernel past the
-    // 256 that two waves per SIMD allow.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int row = ln & 31, lhl = ln >> 5, lgrp = ln >> 4;
-    const int ltr_e = (ln & 15) >> 2, ltr_q = ln & 3;
-
-    // seeds: -log2 LSE and -D of the rows this lane's outputs hold (rows 8 i + 4 hl + j)
+    // (the step functions recompute lane-dependent LDS offsets from an opaque copy of the lane
+    // index in every stage: hoisted out of the loop they would hold ~40 registers and push the
+    // kernel past the 256 that two waves per SIMD allow)
     f32x16 sacc, dacc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(st_lse + 8 * i + 4 * lhl);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st_dlt + 8 * i + 4 * lhl);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sacc[4 * i + j] = -l4[j];
-        dacc[4 * i + j] = -d4[j];
-      }
-    }
-    // S = Q K'^T - LSE and dP - D = dO V^T - D: A operands are rows of the Q / dO tiles
-    {
-      const char* qr = qt + row * (C::QCH * 16);
-      const int swq = swz<C::QCH>(row);
-      const char* orow = ot + row * (C::OCH * 16);
-      const int swo = swz<C::OCH>(row);
-      // chunk (2 ks + hl) ^ sw = 2 ks ^ (hl ^ sw): one xor per k-step on a per-lane constant
-      const unsigned tq = (unsigned)(lhl ^ swq), to = (unsigned)(lhl ^ swo);
-#pragma unroll
-      for (int ks = 0; ks < (C::QK_STEPS > C::DV_STEPS ? C::QK_STEPS : C::DV_STEPS); ++ks) {
-        if (ks < C::QK_STEPS) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + ((tq ^ (2u * ks)) << 4));
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
-        }
-        if (ks < C::DV_STEPS) {
-          // with equal row layouts the dO tile's offsets are the Q tile's plus its size
-          const bf16x8 a = C::QCH == C::OCH
-                               ? *reinterpret_cast<const bf16x8*>(qr + ((tq ^ (2u * ks)) << 4) + C::Q_BYTES)
-                               : *reinterpret_cast<const bf16x8*>(orow + ((to ^ (2u * ks)) << 4));
-          dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dacc, 0, 0, 0);
-        }
-      }
-      // keep each row-fragment read two MFMAs ahead of its use
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int i = 0; i < C::QK_STEPS + C::DV_STEPS - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
+    dkdv_scores<DQK, DV, true>(qt, kf, vf, sacc, dacc);
     // mask where a row does not see the key (or the key is past the tile's valid keys)
     const bool need_mask = load_uniform_i32(blkmin + qb) < kpos0 + C::BKV - 1 || nvalid < C::BKV || (qb + 1) * kBQ > p.Sq;
-    if (need_mask) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int4 q4 = *reinterpret_cast<const int4*>(st_pos + 8 * i + 4 * lhl);
-        const int qp[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sacc[4 * i + j] = (kk < nvalid && kpos <= qp[j]) ? sacc[4 * i + j] : -INFINITY;
-      }
-    }
-    // P and dS, bf16, in the B-operand layout of the two products below (k-step ks: rows
-    // 16 ks + 8 (t / 4) + 4 hl + t % 4 in register t)
     bf16x8 pb[2], dsb[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pr = __builtin_amdgcn_exp2f(sacc[r]);
-      pb[r / 8][r % 8] = (__bf16)pr;
-      dsb[r / 8][r % 8] = (__bf16)(pr * dacc[r]);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS, A operands from transposing reads of the tiles
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    const unsigned cbase = 16u * (unsigned)(lgrp & 1) + 4u * (unsigned)ltr_q;  // column within a 32-block
-    // Column block m adds 4 m to the 16-byte chunk, which only touches chunk bits 2..3, so
-    // (4 m + c) ^ sw = 4 m ^ (c ^ sw); rows 16 further (the next k-step) keep the swizzle.
-    const int row_a0 = 4 * (lgrp >> 1) + ltr_e, row_b0 = row_a0 + 8;
-    const unsigned c0 = cbase >> 3, within = (cbase & 7u) * 2u;
-    const unsigned ta = c0 ^ (unsigned)swz<C::OCH>(row_a0), tb = c0 ^ (unsigned)swz<C::OCH>(row_b0);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int row_a = 16 * ks + row_a0;
-      const int row_b = row_a + 8;
-#pragma unroll
-      for (int m = 0; m < C::MV; ++m) {
-        const char* pa = ot + row_a * (C::OCH * 16) + ((ta ^ (4u * m)) << 4) + within;
-        const char* pb2 = ot + row_b * (C::OCH * 16) + ((tb ^ (4u * m)) << 4) + within;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
-        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[ks], dvacc[m], 0, 0,
-                                                           0);
-      }
-#pragma unroll
-      for (int m = 0; m < C::MK; ++m) {
-        const unsigned qa = C::QCH == C::OCH ? ta : c0 ^ (unsigned)swz<C::QCH>(row_a0);
-        const unsigned qb_ = C::QCH == C::OCH ? tb : c0 ^ (unsigned)swz<C::QCH>(row_b0);
-        const char* pa = qt + row_a * (C::QCH * 16) + ((qa ^ (4u * m)) << 4) + within;
-        const char* pb2 = qt + row_b * (C::QCH * 16) + ((qb_ ^ (4u * m)) << 4) + within;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
-        i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), dsb[ks], dkacc[m], 0, 0,
-                                                           0);
-      }
-    }
-    // keep the transposing reads (two per MFMA) ahead of their MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * (C::MV + C::MK) - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    dkdv_probs<DQK, DV>(qt, need_mask, kk, kpos, nvalid, sacc, dacc, pb, dsb);
+    dkdv_grads<DQK, DV, true>(qt, pb, dsb, dkacc, dvacc);
 
     // the next stage's copies must have landed; the one after may stay in flight
     if (qb2 >= 0)
@@ -689,6 +809,7 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
     h = h1;
     qb1 = qb2;
     h1 = h2;
+  }
   }
 
   // dK = scale dK^T, dV; lane holds key kk, dims 32 m + 8 a4 + 4 hl + t

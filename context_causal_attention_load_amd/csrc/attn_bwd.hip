@@ -21,8 +21,9 @@
 //  * dkdv: key-stationary. A workgroup owns 32 keys per wave of one kv head (256 keys at
 //    Dqk = 128, else 128); the keys' K' (scaled) and V fragments stay in registers as B operands.
 //    It streams (32-row query block, query head) stages of Q, dO, log2-LSE, D and positions
-//    through a 3-stage LDS ring,
-//    skipping blocks whose rows are all before the keys. Per stage: S = Q K'^T seeded with
+//    through an LDS ring (3 slots; at Dqk = 192, where a wave has its SIMD to itself, 6 slots
+//    and two stages per barrier), skipping blocks whose rows are all before the keys.
+//    Per stage: S = Q K'^T seeded with
 //    -LSE, dP - D = dO V^T seeded with -D; P and dS come out with a lane per key, already in
 //    the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS, whose A operands are the
 //    transposing LDS reads of the dO and Q tiles.

@@ -100,11 +100,11 @@ class Prefill:
                                    oatt.permute_ref(self.v, self.seq, cp).double())}
         return self._ref_perm[cp]
 
-    def gpu_rank(self, cp, rank, q_positions=None):
+    def gpu_rank(self, cp, rank, q_positions=None, split=True):
         c = self.seq // (2 * cp)
         kp, vp = self.kv_perm(cp)
         qs = cpa.permute(self.qd, cp, row_begin=rank * 2 * c, row_count=2 * c)
-        o, lse = cpa.attention_fwd(qs, kp, vp, cp, rank, q_positions=q_positions, scale=self.scale)
+        o, lse = cpa.attention_fwd(qs, kp, vp, cp, rank, q_positions=q_positions, scale=self.scale, split=split)
         torch.cuda.synchronize()
         return o, lse
 
@@ -118,9 +118,10 @@ class Prefill:
         return oatt.cp_attention_ref(qs, kp, vp, pos, self.seq, cp, self.scale)
 
 
-def check_rank(pf, cp, rank, rows=None, tag=""):
-    announce(f"{tag} attention_fwd cp={cp} rank={rank} rows={'all' if rows is None else len(rows)}")
-    o, lse = pf.gpu_rank(cp, rank)
+def check_rank(pf, cp, rank, rows=None, tag="", split=True):
+    announce(f"{tag} attention_fwd cp={cp} rank={rank} rows={'all' if rows is None else len(rows)}"
+             f"{'' if split else ' (never split)'}")
+    o, lse = pf.gpu_rank(cp, rank, split=split)
     O_ref, L_ref = pf.oracle_rank(cp, rank, rows)
     o = o.float().cpu().numpy()
     lse = lse.cpu().numpy()

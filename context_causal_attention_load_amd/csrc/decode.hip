@@ -11,10 +11,12 @@
 //    to len_b and all G query heads of g; it writes (max, sum, unnormalised output) partials.
 //    Splits past len_b exit at once, so nothing beyond the valid length is ever loaded.
 //  * Second pass: the partials of each (b, h) are merged with log-sum-exp weights.
-//  * bf16, D = 128, G <= 8 (the fast path): every K and V load of the split is issued before any
-//    arithmetic, so a workgroup keeps its whole 2 x 64 KB split in flight; scores use v_dot2
-//    on bf16 pairs with 4 lanes per key row and a DPP reduction.
-//  * Other cases (fp32 caches, D = 64, G > 8) use a simpler split kernel with the same partial layout.
+//  * bf16, D = 128, G <= 16 (the fast path): every K and V load of the split is issued before
+//    any arithmetic, so a workgroup keeps its whole 2 x 64 KB split in flight; scores use v_dot2
+//    on bf16 pairs with 4 lanes per key row and a DPP reduction. Above 8 heads the heads are
+//    taken in two groups over the same registers.
+//  * Other cases (fp32 caches, D = 64, G > 16) use a simpler split kernel with the same partial
+//    layout.
 //  * The merge is a separate launch: merging inside the split kernel (last workgroup to
 //    arrive) needs a device-scope release per workgroup, which on this part writes back the
 //    whole L2 and costs far more than the second launch.
@@ -374,11 +376,20 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
   constexpr int VS = kFastThreads / LPRV;  // V row slots
   constexpr int VR = SL / VS;              // V rows per lane (consecutive pairs share a v_dot2)
   static_assert(SL % KROWS == 0 && SL % VS == 0 && VR % 2 == 0, "split / thread layout mismatch");
+  // The P V reduction buffer holds HG <= 8 heads; more than 8 query heads per kv head are taken
+  // in NG groups of HG (12 -> 6 + 6, 16 -> 8 + 8) over the same V registers. It shares its LDS
+  // with the scores, which are dead once the probabilities are formed, so 16 heads still fit
+  // three workgroups per CU.
+  constexpr int NG = (G + 7) / 8;
+  constexpr int HG = (G + NG - 1) / NG;
+  constexpr int kRedFloats = kFastWaves * HG * D;
+  constexpr int kScoreFloats = G * SL;
 
-  __shared__ float s_s[G][SL];                                   // scores, log2 units
+  __shared__ float s_sr[kRedFloats > kScoreFloats ? kRedFloats : kScoreFloats];
+  float(*s_s)[SL] = reinterpret_cast<float(*)[SL]>(s_sr);           // scores, log2 units
+  float(*s_red)[HG][D] = reinterpret_cast<float(*)[HG][D]>(s_sr);   // per-wave P V sums
   __shared__ __attribute__((aligned(16))) __bf16 s_pb[G][VS][VR];  // bf16 probabilities by V slot
   __shared__ __attribute__((aligned(16))) __bf16 s_q[G][D];
-  __shared__ float s_red[kFastWaves][G][D];
   __shared__ float s_m[G], s_l[G];
 
   int split, g, b;
@@ -455,12 +466,12 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
   // ---- per-head max / probabilities / sum over the split: one wave per head. Probabilities
   // are rounded to bf16 once; the sum adds the rounded values, and they are stored where the
   // P V step reads them (by V row slot, consecutive rows of a slot adjacent).
-  if (wave < G) {
+  for (int h = wave; h < G; h += kFastWaves) {
     float x[SL / 64];
     float m = -INFINITY;
 #pragma unroll
     for (int j = 0; j < SL / 64; ++j) {
-      x[j] = s_s[wave][lane + 64 * j];
+      x[j] = s_s[h][lane + 64 * j];
       m = fmaxf(m, x[j]);
     }
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -469,13 +480,13 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
     for (int j = 0; j < SL / 64; ++j) {
       const int row = lane + 64 * j;
       const __bf16 e = (__bf16)__builtin_amdgcn_exp2f(x[j] - m);
-      s_pb[wave][row % VS][row / VS] = e;
+      s_pb[h][row % VS][row / VS] = e;
       l += (float)e;
     }
     for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
     if (lane == 0) {
-      s_m[wave] = m;
-      s_l[wave] = l;
+      s_m[h] = m;
+      s_l[h] = l;
     }
   }
   __syncthreads();
@@ -501,43 +512,52 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
   const int rowq = lane / 16;
   const int tsel = (rowq == 0) ? 0 : (rowq == 1 ? 2 : (rowq == 2 ? 1 : 3));
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float a8[8];
+  for (int grp = 0; grp < NG; ++grp) {
+    const int h0 = grp * HG;                   // first query head of the group
+    const int hn = HG < G - h0 ? HG : G - h0;  // heads in the group
+    if (grp > 0) __syncthreads();              // the previous group's partials are read out
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a8[e] = 0.f;
+    for (int hh = 0; hh < HG; ++hh) {
+      if (hh < hn) {
+        float a8[8];
 #pragma unroll
-    for (int pi = 0; pi < VR / 2; ++pi) {
-      const unsigned pw = reinterpret_cast<const unsigned*>(&s_pb[h][vslot][0])[pi];
+        for (int e = 0; e < 8; ++e) a8[e] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a8[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw), as_bf16x2(vp[pi][e]), a8[e], false);
+        for (int pi = 0; pi < VR / 2; ++pi) {
+          const unsigned pw = reinterpret_cast<const unsigned*>(&s_pb[h0 + hh][vslot][0])[pi];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            a8[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw), as_bf16x2(vp[pi][e]), a8[e], false);
+        }
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(a8[2 * i]), __float_as_uint(a8[2 * i + 1]), false,
+                                                     false);
+          hv[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(hv[2 * j]), __float_as_uint(hv[2 * j + 1]), false,
+                                                     false);
+          s_red[wave][hh][vc * 8 + 4 * j + tsel] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+        }
+      }
     }
-    float hv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(a8[2 * i]), __float_as_uint(a8[2 * i + 1]), false,
-                                                 false);
-      hv[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(hv[2 * j]), __float_as_uint(hv[2 * j + 1]), false,
-                                                 false);
-      s_red[wave][h][vc * 8 + 4 * j + tsel] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-    }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- this split's partial: (o[0..D), max, sum) per head
-  for (int idx = tid; idx < G * D; idx += kFastThreads) {
-    const int h = idx / D, d = idx % D;
-    float x = 0.f;
+    // ---- this split's partial: (o[0..D), max, sum) per head of the group
+    for (int idx = tid; idx < hn * D; idx += kFastThreads) {
+      const int hh = idx / D, d = idx % D, h = h0 + hh;
+      float x = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < kFastWaves; ++wv) x += s_red[wv][h][d];
-    float* part = p.ws + (((int64_t)b * p.Hq + g * p.G + h) * p.nsplit + split) * (D + 2);
-    part[d] = x;
-    if (d == 0) {
-      part[D] = s_m[h];
-      part[D + 1] = s_l[h];
+      for (int wv = 0; wv < kFastWaves; ++wv) x += s_red[wv][hh][d];
+      float* part = p.ws + (((int64_t)b * p.Hq + g * p.G + h) * p.nsplit + split) * (D + 2);
+      part[d] = x;
+      if (d == 0) {
+        part[D] = s_m[h];
+        part[D + 1] = s_l[h];
+      }
     }
   }
 }
@@ -558,6 +578,14 @@ bool launch_fast_128(const DecParams& p, hipStream_t stream) {
     case 6: launch_fast<128, 6>(p, stream); return true;
     case 7: launch_fast<128, 7>(p, stream); return true;
     case 8: launch_fast<128, 8>(p, stream); return true;
+    case 9: launch_fast<128, 9>(p, stream); return true;
+    case 10: launch_fast<128, 10>(p, stream); return true;
+    case 11: launch_fast<128, 11>(p, stream); return true;
+    case 12: launch_fast<128, 12>(p, stream); return true;
+    case 13: launch_fast<128, 13>(p, stream); return true;
+    case 14: launch_fast<128, 14>(p, stream); return true;
+    case 15: launch_fast<128, 15>(p, stream); return true;
+    case 16: launch_fast<128, 16>(p, stream); return true;
     default: return false;
   }
 }

@@ -351,7 +351,11 @@ def test_decode_full_workload_with_poisoned_tail():
 
 @pytest.mark.parametrize("batch,hq,hkv,d,max_len,dtype,lens", [
     (4, 48, 8, 128, 2048, torch.bfloat16, [1, 2048, 256, 257]),
-    (3, 16, 1, 128, 300, torch.bfloat16, [300, 1, 255]),     # G=16 > heads per pass
+    (3, 16, 1, 128, 300, torch.bfloat16, [300, 1, 255]),     # G=16: two P V groups of 8
+    (2, 9, 1, 128, 513, torch.bfloat16, [513, 257]),          # G=9: P V groups of 5 and 4
+    (3, 24, 2, 128, 800, torch.bfloat16, [800, 1, 256]),      # G=12: groups of 6 and 6
+    (2, 26, 2, 128, 600, torch.bfloat16, [600, 299]),         # G=13: groups of 7 and 6
+    (2, 17, 1, 128, 300, torch.bfloat16, [300, 45]),          # G=17: the generic kernel
     (2, 8, 8, 64, 513, torch.float32, [513, 17]),
     (5, 12, 4, 64, 1000, torch.bfloat16, [999, 1000, 512, 3, 768]),
     (2, 4, 2, 128, 64, torch.float32, [64, 33]),
@@ -372,6 +376,22 @@ def test_decode_edge_lengths(batch, hq, hkv, d, max_len, dtype, lens):
     tol = TOL[dtype]
     assert_close(o, O_ref, tol, "decode O")
     assert_close(lse, L_ref, tol, "decode LSE")
+
+
+def test_decode_llama405b_shape():
+    """Llama3.1-405B-shaped decode (128 query heads over 8 kv heads, G = 16, D = 128) over
+    8 sequences of mixed length up to 4096, NaN past every length."""
+    announce("decode Llama3.1-405B shape: B=8, Hq=128, Hkv=8, D=128, Lmax=4096")
+    lengths, q, kc, vc = synth.decode_inputs(8, 128, 8, 128, 4096, 1, 4096, torch.bfloat16, seed=405)
+    lengths[0] = 4096
+    scale = 1.0 / math.sqrt(128)
+    O_ref, L_ref = oatt.decode_ref(q, kc, vc, lengths.numpy(), scale)
+    for b in range(8):
+        kc[b, :, lengths[b]:] = float("nan")
+        vc[b, :, lengths[b]:] = float("nan")
+    o, lse = run_decode(lengths, q, kc, vc, scale)
+    assert_close(o, O_ref, 2e-2, "decode O")
+    assert_close(lse, L_ref, 2e-2, "decode LSE")
 
 
 def test_decode_zero_length():

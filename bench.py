@@ -301,7 +301,11 @@ def other_configs_ms(dev, iters=5, bwd_iters=3):
             dq = torch.empty((w.batch, 2 * c, w.hq, w.d_qk), dtype=torch.float32, device=dev)
             dk = torch.empty((w.batch, w.seq, w.hkv, w.d_qk), dtype=torch.float32, device=dev)
             dv = torch.empty((w.batch, w.seq, w.hkv, w.d_v), dtype=torch.float32, device=dev)
-            bws = torch.empty(cpa.attention_bwd_workspace_bytes(w.batch, 2 * c, w.hq), dtype=torch.uint8, device=dev)
+            # the backward's workspace also holds the dQ pieces of heavy row blocks (small grids)
+            bbase = cpa.attention_bwd_workspace_bytes(w.batch, 2 * c, w.hq)
+            bneed = max(cpa.attention_bwd_split_workspace_bytes(w.batch, w.seq, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype,
+                                                                cp, r) for r in range(cp))
+            bws = torch.empty(max(bneed, bbase), dtype=torch.uint8, device=dev)
             ms, bms = [], []
             for r in range(cp):
                 qs = cpa.permute(qd, cp, row_begin=r * 2 * c, row_count=2 * c)
@@ -335,7 +339,9 @@ def other_configs_ms(dev, iters=5, bwd_iters=3):
                         "rank_max_over_mean": round(max(ms) / avg, 4), "heavy_row_blocks_split": need > 0,
                         "useful_flop_per_rank": flops, "tflops": round(tf, 1),
                         "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                        "backward": {"ms_per_rank": [round(x, 3) for x in bms], "useful_flop_per_rank": bflops,
+                        "backward": {"ms_per_rank": [round(x, 3) for x in bms],
+                                     "rank_max_over_mean": round(max(bms) / bavg, 4),
+                                     "heavy_row_blocks_dq_split": bneed > bbase, "useful_flop_per_rank": bflops,
                                      "tflops": round(btf, 1), "frac_of_bf16_peak": round(btf / PEAK_BF16_TFLOPS, 4)}})
             del d_o, dq, dk, dv, bws
         del qd, kd, vd

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     attention_fwd_workspace_bytes,
     attention_bwd,
     attention_bwd_workspace_bytes,
+    attention_bwd_split_workspace_bytes,
     decode,
     decode_noalloc,
     decode_merge,

@@ -75,6 +75,8 @@ def load_library():
                                                 vp, ctypes.c_size_t, vp]
     lib.cp_attention_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.cp_attention_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.cp_attention_bwd_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.cp_attention_bwd_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32]
     lib.cp_attention_bwd.restype = ctypes.c_int
     lib.cp_attention_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                      i32, f32, i32, i32, vp, ctypes.c_size_t, vp]
@@ -384,11 +386,24 @@ def attention_bwd_workspace_bytes(batch, sq, hq):
     return int(load_library().cp_attention_bwd_workspace_bytes(batch, sq, hq))
 
 
+def attention_bwd_split_workspace_bytes(batch, seq, hq, hkv, d_qk, d_v, dtype, cp, rank):
+    """Workspace bytes with which the backward also splits the dQ of heavy row blocks of the
+    rank's own shard (equal to attention_bwd_workspace_bytes(batch, seq // cp, hq) when the shape
+    is not split; 0 for invalid arguments)."""
+    return int(load_library().cp_attention_bwd_split_workspace_bytes(batch, seq, hq, hkv, d_qk, d_v, _DTYPES[dtype],
+                                                                     cp, rank))
+
+
 def attention_bwd(q_shard, k, v, o, lse, d_o, cp, rank, q_positions=None, scale=None, workspace=None, dq=None,
-                  dk=None, dv=None):
+                  dk=None, dv=None, split=True):
     """Backward of attention_fwd for one rank (bf16). Inputs as for attention_fwd plus its O and
     LSE and dO [B, Sq, Hq, Dv]. Returns float32 (dQ [B, Sq, Hq, Dqk], dK [B, S, Hkv, Dqk],
-    dV [B, S, Hkv, Dv]), dK/dV in the gathered key order and holding this rank's share."""
+    dV [B, S, Hkv, Dv]), dK/dV in the gathered key order and holding this rank's share.
+
+    With ``split`` (the default) a new workspace is sized so that a grid too small to balance
+    itself computes dQ of its heavy row blocks in pieces (the library decides from the
+    workspace's size); ``split=False`` sizes it for the unsplit call. A caller's ``workspace``
+    is used as given."""
     _need_gpu(q_shard, k, v, o, lse, d_o, q_positions, workspace, dq, dk, dv)
     if q_shard.dtype != torch.bfloat16 or k.dtype != q_shard.dtype or v.dtype != q_shard.dtype:
         raise ValueError("q, k and v must be bfloat16")
@@ -408,7 +423,10 @@ def attention_bwd(q_shard, k, v, o, lse, d_o, cp, rank, q_positions=None, scale=
         scale = 1.0 / math.sqrt(Dqk)
     dev = q_shard.device
     if workspace is None:
-        workspace = torch.empty(max(attention_bwd_workspace_bytes(B, Sq, Hq), 16), dtype=torch.uint8, device=dev)
+        need = attention_bwd_workspace_bytes(B, Sq, Hq)
+        if split and q_positions is None:
+            need = max(need, attention_bwd_split_workspace_bytes(B, S, Hq, Hkv, Dqk, Dv, q_shard.dtype, cp, rank))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _check_buf(dq, (B, Sq, Hq, Dqk), torch.float32, "dq")
     _check_buf(dk, (B, S, Hkv, Dqk), torch.float32, "dk")
     _check_buf(dv, (B, S, Hkv, Dv), torch.float32, "dv")

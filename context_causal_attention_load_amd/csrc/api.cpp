@@ -247,6 +247,27 @@ size_t cp_attention_bwd_workspace_bytes(int32_t batch, int32_t sq, int32_t hq) {
   return attn_bwd_workspace_bytes(batch, sq, hq);
 }
 
+size_t cp_attention_bwd_split_workspace_bytes(int32_t batch, int32_t seq, int32_t hq, int32_t hkv, int32_t d_qk,
+                                              int32_t d_v, int32_t dtype, int32_t cp, int32_t rank) {
+  if (cp < 1 || seq < 1 || seq % (2 * (int64_t)cp) != 0) return 0;
+  if (fwd_shape_checks("cp_attention_bwd_split_workspace_bytes", batch, seq, seq / cp, hq, hkv, d_qk, d_v, dtype, cp,
+                       rank, false) != CPA_OK)
+    return 0;
+  if (dtype != CPA_BF16 || batch == 0) return 0;
+  AttnBwdArgs a{};
+  a.batch = batch;
+  a.seq = seq;
+  a.sq = seq / cp;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d_qk = d_qk;
+  a.d_v = d_v;
+  a.cp = cp;
+  a.rank = rank;
+  a.scale = 1.f;
+  return attn_bwd_split_workspace_bytes(a);
+}
+
 int cp_attention_bwd(const void* q_shard, const void* k, const void* v, const void* o, const float* lse,
                      const void* d_o, const int32_t* q_positions, float* dq, float* dk, float* dv, int32_t batch,
                      int32_t seq, int32_t sq, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int32_t dtype,
@@ -295,6 +316,7 @@ int cp_attention_bwd(const void* q_shard, const void* k, const void* v, const vo
   a.dk = dk;
   a.dv = dv;
   a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
   a.batch = batch;
   a.seq = seq;
   a.sq = sq;

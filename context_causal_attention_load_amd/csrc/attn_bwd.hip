@@ -171,7 +171,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
   const char* kbase = static_cast<const char*>(p.k) + (int64_t)w.b * p.S * kv_row_bytes_k + (int64_t)w.g * DQK * 2;
   const char* vbase = static_cast<const char*>(p.v) + (int64_t)w.b * p.S * kv_row_bytes_v + (int64_t)w.g * DV * 2;
   const int c = p.c;
-  const int imax = min(qmax / c, 2 * p.cp - 1);
+  // the row block's visible key tiles, or the piece of them this workgroup owns
+  const int tpc = (c + C::BK - 1) / C::BK;
+  int t_beg, t_end;
+  piece_tiles(p, w, visible_tiles(qmax, c, p.cp, C::BK), t_beg, t_end);
 
   // DMA slots: wave-instruction (u, wave) fills LDS bytes [1024 (u kWaves + wave), + 1024) of a
   // tile, lane l at + 16 l, from whichever (row, chunk) the swizzle puts there. The per-lane rows
@@ -245,16 +248,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
     }
   }
 
-  TileCursor tc{0, 0};
-  dma_tile(tc, 0);
+  TileCursor tc{t_beg / tpc, (t_beg % tpc) * C::BK};
+  if (t_beg < t_end) dma_tile(tc, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int buf = 0;
 
-  while (tc.chunk <= imax) {
+  for (int t = t_beg; t < t_end; ++t) {
     TileCursor nx = tc;
     next_tile<C::BK>(nx, c, qmax);
-    const bool has_next = nx.chunk <= imax;
+    const bool has_next = t + 1 < t_end;
     if (has_next) dma_tile(nx, buf ^ 1);
 
     const char* kb = lds + buf * C::STAGE;
@@ -344,7 +347,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
   }
 
   if (my_row < p.Sq) {
+    // a piece of a cut row block writes its share of dQ to its partial slot (the merge adds
+    // the slots); every other work item writes dQ itself
     float* og = e.dq + (((int64_t)w.b * p.Sq + my_row) * p.Hq + head) * DQK;
+    if (w.piece >= 0 && p.piece_slot[w.piece] >= 0) {
+      const int64_t slot = (int64_t)w.unit * p.n_slots + p.piece_slot[w.piece];
+      og = p.part_o + ((slot * p.bm + (my_row - w.row_blk * p.bm)) * p.hpw + wave / p.wpr) * DQK;
+    }
 #pragma unroll
     for (int m = 0; m < C::MQ; ++m) {
 #pragma unroll
@@ -356,6 +365,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
       }
     }
   }
+}
+
+// ------------------------------------------------------------------------------------------
+// dQ of split row blocks (small grids): the dq kernel walks bk-key tiles, and its time is that of
+// its heaviest row block when the grid has about one work item per CU. The shared planner cuts
+// the heavy row blocks' visible tiles into pieces; each piece writes its scaled share of dQ to a
+// slot of the caller's workspace, and this kernel adds a cut row block's slots in piece order
+// (a fixed order, so the result does not depend on timing).
+// ------------------------------------------------------------------------------------------
+constexpr int kDqSplitMinTiles = 16;  // no piece below 1024 keys (64-key tiles)
+
+bool plan_dq_split(const AttnBwdArgs& a, const FwdParams& p, SplitPlan& sp) {
+  if (a.q_pos) return false;
+  return plan_split_tiles(p, 64, kDqSplitMinTiles, sp);
+}
+
+struct DqMergeParams {
+  const float* part;
+  float* dq;
+  int Sq, Hq, Hkv, G, hpw, bm, nhs, n_slots, n_split;
+  unsigned char srb[kSplitMaxRb], sslot[kSplitMaxRb], scnt[kSplitMaxRb];
+};
+
+// Block (unit, cut row block, head of the slice, group of rows); thread (row, 4 dims).
+template <int DQK>
+__global__ __launch_bounds__(256) void attn_bwd_dq_merge_kernel(DqMergeParams m) {
+  constexpr int TPR = DQK / 4;
+  constexpr int RPB = 256 / TPR;
+  int bid = blockIdx.x;
+  const int rgs = (m.bm + RPB - 1) / RPB;
+  const int rg = bid % rgs;
+  bid /= rgs;
+  const int lh = bid % m.hpw;
+  bid /= m.hpw;
+  const int j = bid % m.n_split;
+  const int unit = bid / m.n_split;
+  const int lrow = rg * RPB + threadIdx.x / TPR;
+  const int dq = threadIdx.x % TPR;
+  const int row = m.srb[j] * m.bm + lrow;
+  if (lrow >= m.bm || row >= m.Sq) return;
+  const int hs = unit % m.nhs, bg = unit / m.nhs;
+  const int g = bg % m.Hkv, b = bg / m.Hkv;
+  const int head = g * m.G + hs * m.hpw + lh;
+  const int64_t slot0 = (int64_t)unit * m.n_slots + m.sslot[j];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < m.scnt[j]; ++i) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(m.part + (((slot0 + i) * m.bm + lrow) * m.hpw + lh) * DQK + 4 * dq);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += x[e];
+  }
+  *reinterpret_cast<f32x4*>(m.dq + (((int64_t)b * m.Sq + row) * m.Hq + head) * DQK + 4 * dq) = acc;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -879,10 +939,44 @@ hipError_t launch_bwd_typed(const AttnBwdArgs& a, hipStream_t stream) {
   e.pos = reinterpret_cast<int32_t*>(ws + 2 * stat_bytes);
   e.blk = reinterpret_cast<int32_t*>(ws + 2 * stat_bytes + (size_t)Sqp * 4);
 
+  // dQ of heavy row blocks in pieces when the grid is small and the workspace holds the slots
+  FwdParams pq = p;
+  SplitPlan sp;
+  const size_t base = attn_bwd_workspace_bytes(a.batch, a.sq, a.hq);
+  const bool split = plan_dq_split(a, p, sp) &&
+                     a.ws_bytes >= base + split_slot_count(p, sp) * (size_t)p.bm * p.hpw * DQK * sizeof(float);
+  if (split) {
+    apply_split(pq, sp);
+    pq.part_o = reinterpret_cast<float*>(ws + base);
+  }
+
   hipLaunchKernelGGL(bwd_positions_kernel, dim3((Sqp + 255) / 256), dim3(256), 0, stream, p, e);
   const int64_t rows = (int64_t)a.batch * a.hq * Sqp;
   hipLaunchKernelGGL((bwd_delta_kernel<DV>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p, e);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV>), dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, stream, p, e);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV>), dim3((split ? pq.n_items : pq.per_xcd) * kNumXcd), dim3(kThreads),
+                     0, stream, pq, e);
+  if (split) {
+    DqMergeParams m;
+    m.part = pq.part_o;
+    m.dq = a.dq;
+    m.Sq = p.Sq;
+    m.Hq = p.Hq;
+    m.Hkv = p.Hkv;
+    m.G = p.G;
+    m.hpw = p.hpw;
+    m.bm = p.bm;
+    m.nhs = p.nhs;
+    m.n_slots = sp.n_slots;
+    m.n_split = sp.n_split;
+    for (int j = 0; j < sp.n_split; ++j) {
+      m.srb[j] = sp.srb[j];
+      m.sslot[j] = sp.sslot[j];
+      m.scnt[j] = sp.scnt[j];
+    }
+    const int rpb = 256 / (DQK / 4);
+    const int64_t blocks = (int64_t)p.B * p.Hkv * p.nhs * sp.n_split * p.hpw * ((p.bm + rpb - 1) / rpb);
+    hipLaunchKernelGGL(attn_bwd_dq_merge_kernel<DQK>, dim3((unsigned)blocks), dim3(256), 0, stream, m);
+  }
 
   DkvParams d;
   d.B = a.batch;
@@ -909,7 +1003,28 @@ hipError_t launch_bwd_typed(const AttnBwdArgs& a, hipStream_t stream) {
 
 size_t attn_bwd_workspace_bytes(int batch, int sq, int hq) {
   const size_t sqp = ((size_t)sq + kBQ - 1) / kBQ * kBQ;
-  return 2 * (size_t)batch * hq * sqp * 4 + sqp * 4 + 2 * (sqp / kBQ) * 4;
+  const size_t bytes = 2 * (size_t)batch * hq * sqp * 4 + sqp * 4 + 2 * (sqp / kBQ) * 4;
+  return (bytes + 255) / 256 * 256;  // the dQ partial slots of a split start 256-byte aligned
+}
+
+size_t attn_bwd_split_workspace_bytes(const AttnBwdArgs& a) {
+  AttnArgs fa{};
+  fa.q_pos = a.q_pos;
+  fa.batch = a.batch;
+  fa.seq = a.seq;
+  fa.sq = a.sq;
+  fa.hq = a.hq;
+  fa.hkv = a.hkv;
+  fa.d_qk = a.d_qk;
+  fa.d_v = a.d_v;
+  fa.cp = a.cp;
+  fa.rank = a.rank;
+  fa.scale = a.scale;
+  const FwdParams p = make_params(fa);
+  SplitPlan sp;
+  const size_t base = attn_bwd_workspace_bytes(a.batch, a.sq, a.hq);
+  if (p.n_items == 0 || !plan_dq_split(a, p, sp)) return base;
+  return base + split_slot_count(p, sp) * (size_t)p.bm * p.hpw * a.d_qk * sizeof(float);
 }
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {

@@ -114,13 +114,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
 
   // the row block's visible key tiles, or the piece of them this workgroup owns
   const int tpc = (c + C::BK - 1) / C::BK;
-  int t_beg = 0, t_end = visible_tiles(qmax, c, p.cp, C::BK);
-  if (w.piece >= 0) {
-    const int n = p.piece_cnt[w.piece], i = p.piece_idx[w.piece];
-    const int T = t_end;
-    t_beg = i * T / n;
-    t_end = (i + 1) * T / n;
-  }
+  int t_beg, t_end;
+  piece_tiles(p, w, visible_tiles(qmax, c, p.cp, C::BK), t_beg, t_end);
 
   // DMA slots: wave-instruction (u, wave) fills LDS bytes [1024*(u*kWaves + wave), +1024) of a
   // tile, lane l at +16*l; the lane loads whichever (row, chunk) the swizzle puts there. For a
@@ -566,70 +561,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(FwdParams p) 
 }
 
 // ------------------------------------------------------------------------------------------
-// Key-range split of heavy row blocks
+// Key-range split of heavy row blocks (planned by plan_split_tiles): pieces of a cut row block
+// write unnormalised partials and a merge kernel combines them by their running maxima (as the
+// decode does).
 // ------------------------------------------------------------------------------------------
-// A rank's time is that of its busiest compute unit. With at least two work items per CU the
-// heavy-first order evens the CUs out; below that (the 8192-token shape at cp = 4 has one 256-row
-// block per CU, and its heaviest block sees 64 key tiles against 33 on average) the heaviest
-// row block sets the time. There the visible key tiles of each row block are cut into pieces of
-// about the same size, each piece a work item; pieces of a cut row block write unnormalised
-// partials and a merge kernel combines them by their running maxima (as the decode does).
-constexpr int kSplitBelowItems = 512;   // plan a split only for grids with fewer work items
-constexpr int kSplitTargetItems = 256;  // pieces no smaller than the grid's tiles per CU
-constexpr int kSplitMinTiles = 8;       // no piece below this many key tiles
-
-struct SplitPlan {
-  int n_pieces = 0, n_slots = 0, n_split = 0;
-  unsigned char rb[kSplitMaxPieces], idx[kSplitMaxPieces], cnt[kSplitMaxPieces];
-  signed char slot[kSplitMaxPieces];
-  unsigned char srb[kSplitMaxRb], sslot[kSplitMaxRb], scnt[kSplitMaxRb];  // cut row blocks
-};
-
 int bf16_tile_keys(int d_qk, int d_v) { return (2 * 128 * (d_qk + d_v) * 2 <= 128 * 1024) ? 128 : 64; }
 
-// The plan needs the rows' positions on the host, so it is made only for the rank's own shard
-// (positions from cp and rank).
+constexpr int kSplitMinTiles = 8;  // no piece below this many key tiles
+
 bool plan_split(const AttnArgs& a, const FwdParams& p, SplitPlan& sp) {
-  if (a.q_pos || p.n_items >= kSplitBelowItems || p.nrb > kSplitMaxRb) return false;
-  const int bk = bf16_tile_keys(a.d_qk, a.d_v);
-  int T[kSplitMaxRb];
-  int64_t total = 0;
-  for (int rb = 0; rb < p.nrb; ++rb) {
-    const int last_row = std::min(p.Sq, (rb + 1) * p.bm) - 1;
-    const int qmax = (int)std::min<int64_t>(lb_src((int64_t)p.rank * 2 * p.c + last_row, p.c, p.cp), p.S - 1);
-    T[rb] = visible_tiles(qmax, p.c, p.cp, bk);
-    total += T[rb];
-  }
-  const int64_t units = (int64_t)p.B * p.Hkv * p.nhs;
-  const int tau = (int)std::max<int64_t>(kSplitMinTiles, (total * units + kSplitTargetItems - 1) / kSplitTargetItems);
-  int k = 0, slot = 0;
-  for (int rb = p.nrb - 1; rb >= 0; --rb) {  // heaviest (latest positions) first
-    const int n = std::max(1, std::min((T[rb] + tau - 1) / tau, 127));
-    if (k + n > kSplitMaxPieces) return false;
-    for (int i = 0; i < n; ++i, ++k) {
-      sp.rb[k] = (unsigned char)rb;
-      sp.idx[k] = (unsigned char)i;
-      sp.cnt[k] = (unsigned char)n;
-      sp.slot[k] = (signed char)(n > 1 ? slot + i : -1);
-    }
-    if (n > 1) {
-      if (slot + n > 127) return false;
-      sp.srb[sp.n_split] = (unsigned char)rb;
-      sp.sslot[sp.n_split] = (unsigned char)slot;
-      sp.scnt[sp.n_split] = (unsigned char)n;
-      ++sp.n_split;
-      slot += n;
-    }
-  }
-  if (sp.n_split == 0) return false;
-  sp.n_pieces = k;
-  sp.n_slots = slot;
-  return true;
+  if (a.q_pos) return false;
+  return plan_split_tiles(p, bf16_tile_keys(a.d_qk, a.d_v), kSplitMinTiles, sp);
 }
 
 size_t split_workspace_bytes(const FwdParams& p, const SplitPlan& sp, int d_v) {
-  const size_t units = (size_t)p.B * p.Hkv * p.nhs;
-  return units * sp.n_slots * ((size_t)p.bm * p.hpw * d_v + (size_t)p.hpw * p.bm * 2) * sizeof(float);
+  return split_slot_count(p, sp) * ((size_t)p.bm * p.hpw * d_v + (size_t)p.hpw * p.bm * 2) * sizeof(float);
 }
 
 struct SplitMergeParams {
@@ -700,18 +646,9 @@ hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
   SplitPlan sp;
   const bool split = a.ws && plan_split(a, p, sp) && a.ws_bytes >= split_workspace_bytes(p, sp, a.d_v);
   if (split) {
-    p.n_pieces = sp.n_pieces;
-    p.n_slots = sp.n_slots;
+    apply_split(p, sp);
     p.part_o = static_cast<float*>(a.ws);
-    p.part_ml = p.part_o + (size_t)p.B * p.Hkv * p.nhs * sp.n_slots * p.bm * p.hpw * a.d_v;
-    for (int k = 0; k < sp.n_pieces; ++k) {
-      p.piece_rb[k] = sp.rb[k];
-      p.piece_idx[k] = sp.idx[k];
-      p.piece_cnt[k] = sp.cnt[k];
-      p.piece_slot[k] = sp.slot[k];
-    }
-    p.per_xcd = (p.B * p.Hkv + kNumXcd - 1) / kNumXcd;  // (batch, kv head) pairs per XCD
-    p.n_items = p.per_xcd * p.nhs * sp.n_pieces;         // workgroups per XCD
+    p.part_ml = p.part_o + split_slot_count(p, sp) * p.bm * p.hpw * a.d_v;
   }
   dim3 grid((split ? p.n_items : p.per_xcd) * kNumXcd), block(kThreads);
   if (a.d_qk == 128 && a.d_v == 128) {

@@ -4,6 +4,8 @@
 // wave reductions. Internal to libcpattn.so.
 #pragma once
 
+#include <algorithm>
+
 #include "common.h"
 
 namespace cpattn {
@@ -17,10 +19,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
 
-// Key-range split of the forward's heavy row blocks (small grids only): a plan lists, for each
-// (batch, kv head, head slice) unit, its pieces heaviest first; a piece is a range of a row
-// block's visible key tiles. Row blocks cut into several pieces write partials to the caller's
-// workspace and a merge kernel combines them.
+// Key-range split of heavy row blocks (small grids only; the forward and the backward's dQ): a
+// plan lists, for each (batch, kv head, head slice) unit, its pieces heaviest first; a piece is a
+// range of a row block's visible key tiles. Row blocks cut into several pieces write partials to
+// the caller's workspace and a merge kernel combines them.
 constexpr int kSplitMaxPieces = 96;
 constexpr int kSplitMaxRb = 64;
 
@@ -210,6 +212,92 @@ inline FwdParams make_params(const AttnArgs& a) {
   p.part_o = nullptr;
   p.part_ml = nullptr;
   return p;
+}
+
+// ---- split plan (host)
+// A rank's time is that of its busiest compute unit. With at least two work items per CU the
+// heavy-first order evens the CUs out; below that (the 8192-token shape at cp = 4 has one 256-row
+// block per CU, and its heaviest block sees twice the keys of the average one) the heaviest row
+// block sets the time. There the visible key tiles of each row block are cut into pieces of
+// about the same size, each piece a work item.
+constexpr int kSplitBelowItems = 512;   // plan a split only for grids with fewer work items
+constexpr int kSplitTargetItems = 256;  // pieces no smaller than the grid's tiles per CU
+
+struct SplitPlan {
+  int n_pieces = 0, n_slots = 0, n_split = 0;
+  unsigned char rb[kSplitMaxPieces], idx[kSplitMaxPieces], cnt[kSplitMaxPieces];
+  signed char slot[kSplitMaxPieces];
+  unsigned char srb[kSplitMaxRb], sslot[kSplitMaxRb], scnt[kSplitMaxRb];  // cut row blocks
+};
+
+// Plans the split of the rank's own shard (positions from cp and rank: the plan needs them on
+// the host) for a kernel that walks bk-key tiles, with no piece below min_tiles tiles. False when
+// the grid has enough work items, the plan would not fit its tables, or no row block is cut.
+inline bool plan_split_tiles(const FwdParams& p, int bk, int min_tiles, SplitPlan& sp) {
+  if (p.n_items >= kSplitBelowItems || p.nrb > kSplitMaxRb) return false;
+  int T[kSplitMaxRb];
+  int64_t total = 0;
+  for (int rb = 0; rb < p.nrb; ++rb) {
+    const int last_row = std::min(p.Sq, (rb + 1) * p.bm) - 1;
+    const int qmax = (int)std::min<int64_t>(lb_src((int64_t)p.rank * 2 * p.c + last_row, p.c, p.cp), p.S - 1);
+    T[rb] = visible_tiles(qmax, p.c, p.cp, bk);
+    total += T[rb];
+  }
+  const int64_t units = (int64_t)p.B * p.Hkv * p.nhs;
+  const int tau = (int)std::max<int64_t>(min_tiles, (total * units + kSplitTargetItems - 1) / kSplitTargetItems);
+  int k = 0, slot = 0;
+  for (int rb = p.nrb - 1; rb >= 0; --rb) {  // heaviest (latest positions) first
+    const int n = std::max(1, std::min((T[rb] + tau - 1) / tau, 127));
+    if (k + n > kSplitMaxPieces) return false;
+    for (int i = 0; i < n; ++i, ++k) {
+      sp.rb[k] = (unsigned char)rb;
+      sp.idx[k] = (unsigned char)i;
+      sp.cnt[k] = (unsigned char)n;
+      sp.slot[k] = (signed char)(n > 1 ? slot + i : -1);
+    }
+    if (n > 1) {
+      if (slot + n > 127) return false;
+      sp.srb[sp.n_split] = (unsigned char)rb;
+      sp.sslot[sp.n_split] = (unsigned char)slot;
+      sp.scnt[sp.n_split] = (unsigned char)n;
+      ++sp.n_split;
+      slot += n;
+    }
+  }
+  if (sp.n_split == 0) return false;
+  sp.n_pieces = k;
+  sp.n_slots = slot;
+  return true;
+}
+
+// Partial slots of a plan: (batch, kv head, head slice) units x slots.
+inline size_t split_slot_count(const FwdParams& p, const SplitPlan& sp) {
+  return (size_t)p.B * p.Hkv * p.nhs * sp.n_slots;
+}
+
+// Switches the work decomposition to the plan's pieces (decode_item then walks them).
+inline void apply_split(FwdParams& p, const SplitPlan& sp) {
+  p.n_pieces = sp.n_pieces;
+  p.n_slots = sp.n_slots;
+  for (int k = 0; k < sp.n_pieces; ++k) {
+    p.piece_rb[k] = sp.rb[k];
+    p.piece_idx[k] = sp.idx[k];
+    p.piece_cnt[k] = sp.cnt[k];
+    p.piece_slot[k] = sp.slot[k];
+  }
+  p.per_xcd = (p.B * p.Hkv + kNumXcd - 1) / kNumXcd;  // (batch, kv head) pairs per XCD
+  p.n_items = p.per_xcd * p.nhs * sp.n_pieces;         // workgroups per XCD
+}
+
+// The range [t_beg, t_end) of a row block's T visible tiles that a work item owns.
+__device__ __forceinline__ void piece_tiles(const FwdParams& p, const WorkItem& w, int T, int& t_beg, int& t_end) {
+  t_beg = 0;
+  t_end = T;
+  if (w.piece >= 0) {
+    const int n = p.piece_cnt[w.piece], i = p.piece_idx[w.piece];
+    t_beg = i * T / n;
+    t_end = (i + 1) * T / n;
+  }
 }
 
 }  // namespace

@@ -105,11 +105,15 @@ struct AttnBwdArgs {
   float* dq;              // [B, Sq, Hq, Dqk]
   float* dk;              // [B, S, Hkv, Dqk]
   float* dv;              // [B, S, Hkv, Dv]
-  void* ws;               // attn_bwd_workspace_bytes(batch, sq, hq) bytes
+  void* ws;               // at least attn_bwd_workspace_bytes(batch, sq, hq) bytes
+  size_t ws_bytes;        // with attn_bwd_split_workspace_bytes(...) or more, dQ is split
   int batch, seq, sq, hq, hkv, d_qk, d_v, cp, rank;
   float scale;
 };
 size_t attn_bwd_workspace_bytes(int batch, int sq, int hq);
+// Workspace with which the backward also splits the dq kernel's heavy row blocks (small grids,
+// the rank's own shard); attn_bwd_workspace_bytes when the shape is not split.
+size_t attn_bwd_split_workspace_bytes(const AttnBwdArgs& a);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream);
 
 struct DecodeArgs {

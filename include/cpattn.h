@@ -174,11 +174,25 @@ int cp_attention_fwd_ws(const void* q_shard, const void* k, const void* v,
  *   dk, dv   [B, seq, Hkv, Dqk | Dv] float32 (output), in the gathered key order
  *   workspace, workspace_bytes: at least cp_attention_bwd_workspace_bytes(batch, sq, hq) bytes of
  *            caller-owned device scratch; contents on entry do not matter; calls sharing one
- *            workspace must not overlap.
+ *            workspace must not overlap. With at least
+ *            cp_attention_bwd_split_workspace_bytes(...) bytes (and q_positions == NULL), a grid
+ *            too small to balance itself (the 8192-token shape at cp = 4) also computes dQ of its
+ *            heavy 256-row blocks in pieces of their key range, which this workspace holds until a
+ *            last kernel adds them in a fixed order; the ranks then take about equal time (the
+ *            balance in time that "Add context parallelism" asks of the shards). A smaller
+ *            workspace runs unsplit; both give dQ to within float32 rounding of each other.
  * Supported: bf16 with (d_qk, d_v) in {(64, 64), (128, 128), (192, 128)}; CPA_ENOTSUP otherwise. CPA_EINVAL
  * for the forward's argument errors, null pointers (all tensors are required), tensors not
  * 16-byte aligned (lse and q_positions: 4-byte), or a workspace that is too small. */
 size_t cp_attention_bwd_workspace_bytes(int32_t batch, int32_t sq, int32_t hq);
+
+/* cp_attention_bwd_split_workspace_bytes: the workspace bytes with which cp_attention_bwd also
+ * splits the dQ of heavy row blocks for the rank's own shard of this shape (sq = seq / cp); equal
+ * to cp_attention_bwd_workspace_bytes(batch, seq / cp, hq) when the shape is not split (grids
+ * with enough work items); 0 when the arguments are invalid or unsupported. */
+size_t cp_attention_bwd_split_workspace_bytes(int32_t batch, int32_t seq, int32_t hq, int32_t hkv,
+                                              int32_t d_qk, int32_t d_v, int32_t dtype, int32_t cp,
+                                              int32_t rank);
 
 int cp_attention_bwd(const void* q_shard, const void* k, const void* v, const void* o, const float* lse,
                      const void* d_o, const int32_t* q_positions, float* dq, float* dk, float* dv,

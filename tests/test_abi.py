@@ -3,6 +3,7 @@ index helper agrees with the oracle's independent construction, and every argume
 fails with the documented status before any HIP call."""
 
 import ctypes
+import math
 import os
 import re
 
@@ -40,7 +41,7 @@ def test_header_declares_the_boundary():
                  "gqa_decode_attention", "gqa_decode_workspace_bytes", "cpattn_last_error",
                  "cp_load_balance_source_index", "cp_load_balance_positions", "gqa_decode_merge",
                  "gqa_decode_attention_int8kv", "kv_cache_quantize_int8", "cp_attention_bwd",
-                 "cp_attention_bwd_workspace_bytes"):
+                 "cp_attention_bwd_workspace_bytes", "cp_attention_bwd_split_workspace_bytes"):
         assert must in names, names
 
 
@@ -141,6 +142,59 @@ def test_attention_fwd_workspace_bytes(lib):
     assert lib.cp_attention_fwd_workspace_bytes(1, 2048, 1, 1, 128, 128, bf16, 2, 2) == 0
 
 
+def _dq_split_bytes_expected(batch, seq, hq, hkv, d_qk, cp, rank):
+    """The dQ split's workspace restated from its rules: 256-row blocks (MHA: one head per
+    workgroup), 64-key tiles, split only below 512 work items; pieces of tau = max(16, tiles x
+    units / 256) tiles; one partial slot per piece of every cut row block."""
+    c = seq // (2 * cp)
+    sq = 2 * c
+    sqp = -(-sq // 32) * 32
+    base = 2 * batch * hq * sqp * 4 + sqp * 4 + 2 * (sqp // 32) * 4
+    base = -(-base // 256) * 256
+    g = hq // hkv
+    hpw = math.gcd(g, 8)
+    bm = 32 * (8 // hpw)
+    nrb = -(-sq // bm)
+    units = batch * hkv * (g // hpw)
+    if units * nrb >= 512:
+        return base
+    pos = olb.shard_positions(seq, cp, rank)
+    tpc = -(-c // 64)
+    tiles = []
+    for rb in range(nrb):
+        qmax = int(pos[min(sq, (rb + 1) * bm) - 1])
+        imax = min(qmax // c, 2 * cp - 1)
+        tiles.append(imax * tpc + min(-(-(qmax - imax * c + 1) // 64), tpc))
+    tau = max(16, -(-(sum(tiles) * units) // 256))
+    slots = sum(n for n in (-(-t_ // tau) for t_ in tiles) if n > 1)
+    if slots == 0:
+        return base
+    return base + units * slots * bm * hpw * d_qk * 4
+
+
+def test_attention_bwd_split_workspace_bytes(lib):
+    # the 8192-token MHA shape at cp = 4 (256 work items) splits dQ on every rank; the cp = 1
+    # and 131072-token shapes have enough work items and need only the base workspace
+    bf16, f32 = binding.CPA_BF16, binding.CPA_F32
+    for r in range(4):
+        got = lib.cp_attention_bwd_split_workspace_bytes(1, 8192, 32, 32, 128, 128, bf16, 4, r)
+        assert got == _dq_split_bytes_expected(1, 8192, 32, 32, 128, 4, r), r
+        assert got > lib.cp_attention_bwd_workspace_bytes(1, 2048, 32), r
+    for args in ((1, 8192, 32, 32, 128, 128, bf16, 1, 0), (1, 131072, 64, 8, 128, 128, bf16, 8, 3),
+                 (1, 32768, 128, 128, 192, 128, bf16, 4, 0)):
+        b, s, hq, hkv, dqk, dv, dt, cp, r = args
+        got = lib.cp_attention_bwd_split_workspace_bytes(*args)
+        assert got == lib.cp_attention_bwd_workspace_bytes(b, s // cp, hq) == _dq_split_bytes_expected(
+            b, s, hq, hkv, dqk, cp, r), args
+    # a ragged small GQA shape: batch 2, 8 kv heads of 2 query heads
+    assert lib.cp_attention_bwd_split_workspace_bytes(2, 4096, 16, 8, 64, 64, bf16, 2, 1) == \
+        _dq_split_bytes_expected(2, 4096, 16, 8, 64, 2, 1)
+    for bad in ((1, 2048, 1, 1, 128, 128, f32, 1, 0), (1, 2047, 1, 1, 128, 128, bf16, 1, 0),
+                (1, 2048, 1, 1, 96, 96, bf16, 1, 0), (1, 2048, 1, 1, 128, 128, bf16, 2, 2),
+                (0, 2048, 1, 1, 128, 128, bf16, 1, 0), (1, 2048, 3, 2, 128, 128, bf16, 1, 0)):
+        assert lib.cp_attention_bwd_split_workspace_bytes(*bad) == 0, bad
+
+
 def test_attention_fwd_ws_argument_errors(lib):
     rc = lib.cp_attention_fwd_ws(FAKE, FAKE, FAKE, None, FAKE, None, 1, 8192, 2048, 32, 32, 128, 128,
                                  binding.CPA_BF16, 0.088, 4, 0, ctypes.c_void_p(4100), 1 << 30, None)
@@ -193,9 +247,12 @@ def test_attention_bwd_empty_is_ok_without_device(lib):
 
 
 def test_attention_bwd_workspace_size(lib):
-    # log2-LSE and D per (b, h, padded row), positions per padded row, min/max per 32-row block
-    assert cpa.attention_bwd_workspace_bytes(1, 16384, 64) == 2 * 64 * 16384 * 4 + 16384 * 4 + 2 * 512 * 4
-    assert cpa.attention_bwd_workspace_bytes(2, 100, 4) == 2 * 2 * 4 * 128 * 4 + 128 * 4 + 2 * 4 * 4
+    # log2-LSE and D per (b, h, padded row), positions per padded row, min/max per 32-row block,
+    # rounded up to 256 bytes (where the dQ split's partial slots begin)
+    def up256(n):
+        return -(-n // 256) * 256
+    assert cpa.attention_bwd_workspace_bytes(1, 16384, 64) == up256(2 * 64 * 16384 * 4 + 16384 * 4 + 2 * 512 * 4)
+    assert cpa.attention_bwd_workspace_bytes(2, 100, 4) == up256(2 * 2 * 4 * 128 * 4 + 128 * 4 + 2 * 4 * 4)
     assert cpa.attention_bwd_workspace_bytes(0, 100, 4) == 0
 
 

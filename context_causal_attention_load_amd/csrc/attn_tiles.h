@@ -36,8 +36,9 @@ struct FwdParams {
   int B, S, Sq, Hq, Hkv, G, cp, c, rank;
   int hpw, wpr, bm, nrb, nhs, n_items, per_xcd;
   float scale_log2;
-  // split plan (n_pieces == 0: one item per row block, no partials)
-  int n_pieces, n_slots;
+  // split plan (n_pieces == 0: one item per row block, no partials); piece i of a cut row block
+  // owns its visible tiles [i tau, min((i + 1) tau, T))
+  int n_pieces, n_slots, tau;
   float* part_o;   // [unit, slot, bm rows, hpw heads, Dv] unnormalised outputs
   float* part_ml;  // [unit, slot, hpw heads, bm rows, 2] running max (log2 units) and row sum
   unsigned char piece_rb[kSplitMaxPieces];   // row block of each piece
@@ -209,6 +210,7 @@ inline FwdParams make_params(const AttnArgs& a) {
   p.scale_log2 = a.scale * kLog2e;
   p.n_pieces = 0;
   p.n_slots = 0;
+  p.tau = 0;
   p.part_o = nullptr;
   p.part_ml = nullptr;
   return p;
@@ -218,21 +220,25 @@ inline FwdParams make_params(const AttnArgs& a) {
 // A rank's time is that of its busiest compute unit. With at least two work items per CU the
 // heavy-first order evens the CUs out; below that (the 8192-token shape at cp = 4 has one 256-row
 // block per CU, and its heaviest block sees twice the keys of the average one) the heaviest row
-// block sets the time. There the visible key tiles of each row block are cut into pieces of
-// about the same size, each piece a work item.
+// block sets the time. There the visible key tiles of the heavy row blocks are cut into pieces,
+// each piece a work item.
 constexpr int kSplitBelowItems = 512;   // plan a split only for grids with fewer work items
 constexpr int kSplitTargetItems = 256;  // pieces no smaller than the grid's tiles per CU
 
 struct SplitPlan {
-  int n_pieces = 0, n_slots = 0, n_split = 0;
+  int n_pieces = 0, n_slots = 0, n_split = 0, tau = 0;
   unsigned char rb[kSplitMaxPieces], idx[kSplitMaxPieces], cnt[kSplitMaxPieces];
   signed char slot[kSplitMaxPieces];
   unsigned char srb[kSplitMaxRb], sslot[kSplitMaxRb], scnt[kSplitMaxRb];  // cut row blocks
 };
 
 // Plans the split of the rank's own shard (positions from cp and rank: the plan needs them on
-// the host) for a kernel that walks bk-key tiles, with no piece below min_tiles tiles. False when
-// the grid has enough work items, the plan would not fit its tables, or no row block is cut.
+// the host) for a kernel that walks bk-key tiles. tau, the tiles per CU if the rank's work were
+// spread evenly (no less than min_tiles), bounds a work item: a row block of T > tau tiles is cut
+// into pieces of tau tiles and a remainder, and the pieces are dispatched largest first, so the
+// remainders and the small row blocks fill the CUs that free first and every CU ends near tau.
+// False when the grid has enough work items, the plan would not fit its tables, or no row block
+// is cut.
 inline bool plan_split_tiles(const FwdParams& p, int bk, int min_tiles, SplitPlan& sp) {
   if (p.n_items >= kSplitBelowItems || p.nrb > kSplitMaxRb) return false;
   int T[kSplitMaxRb];
@@ -246,8 +252,8 @@ inline bool plan_split_tiles(const FwdParams& p, int bk, int min_tiles, SplitPla
   const int64_t units = (int64_t)p.B * p.Hkv * p.nhs;
   const int tau = (int)std::max<int64_t>(min_tiles, (total * units + kSplitTargetItems - 1) / kSplitTargetItems);
   int k = 0, slot = 0;
-  for (int rb = p.nrb - 1; rb >= 0; --rb) {  // heaviest (latest positions) first
-    const int n = std::max(1, std::min((T[rb] + tau - 1) / tau, 127));
+  for (int rb = p.nrb - 1; rb >= 0; --rb) {  // latest positions (heaviest row blocks) first
+    const int n = (T[rb] + tau - 1) / tau;
     if (k + n > kSplitMaxPieces) return false;
     for (int i = 0; i < n; ++i, ++k) {
       sp.rb[k] = (unsigned char)rb;
@@ -267,6 +273,28 @@ inline bool plan_split_tiles(const FwdParams& p, int bk, int min_tiles, SplitPla
   if (sp.n_split == 0) return false;
   sp.n_pieces = k;
   sp.n_slots = slot;
+  sp.tau = tau;
+  // Dispatch the pieces largest first (workgroups start in list order, each on the CU that frees
+  // first). A piece keeps its slot, so the merge's order, and with it the result, does not change.
+  int order[kSplitMaxPieces], size[kSplitMaxPieces];
+  for (int i = 0; i < k; ++i) {
+    const int j = sp.idx[i];
+    size[i] = std::min(T[sp.rb[i]], (j + 1) * tau) - j * tau;
+    order[i] = i;
+  }
+  std::stable_sort(order, order + k, [&](int a, int b) { return size[a] > size[b]; });
+  unsigned char rb[kSplitMaxPieces], idx[kSplitMaxPieces], cnt[kSplitMaxPieces];
+  signed char sl[kSplitMaxPieces];
+  for (int i = 0; i < k; ++i) {
+    rb[i] = sp.rb[order[i]];
+    idx[i] = sp.idx[order[i]];
+    cnt[i] = sp.cnt[order[i]];
+    sl[i] = sp.slot[order[i]];
+  }
+  std::copy(rb, rb + k, sp.rb);
+  std::copy(idx, idx + k, sp.idx);
+  std::copy(cnt, cnt + k, sp.cnt);
+  std::copy(sl, sl + k, sp.slot);
   return true;
 }
 
@@ -279,6 +307,7 @@ inline size_t split_slot_count(const FwdParams& p, const SplitPlan& sp) {
 inline void apply_split(FwdParams& p, const SplitPlan& sp) {
   p.n_pieces = sp.n_pieces;
   p.n_slots = sp.n_slots;
+  p.tau = sp.tau;
   for (int k = 0; k < sp.n_pieces; ++k) {
     p.piece_rb[k] = sp.rb[k];
     p.piece_idx[k] = sp.idx[k];
@@ -289,14 +318,14 @@ inline void apply_split(FwdParams& p, const SplitPlan& sp) {
   p.n_items = p.per_xcd * p.nhs * sp.n_pieces;         // workgroups per XCD
 }
 
-// The range [t_beg, t_end) of a row block's T visible tiles that a work item owns.
+// The range [t_beg, t_end) of a row block's T visible tiles that a work item owns (the host
+// plans from the same T, so a piece's range is never empty).
 __device__ __forceinline__ void piece_tiles(const FwdParams& p, const WorkItem& w, int T, int& t_beg, int& t_end) {
   t_beg = 0;
   t_end = T;
-  if (w.piece >= 0) {
-    const int n = p.piece_cnt[w.piece], i = p.piece_idx[w.piece];
-    t_beg = i * T / n;
-    t_end = (i + 1) * T / n;
+  if (w.piece >= 0 && p.piece_cnt[w.piece] > 1) {
+    t_beg = p.piece_idx[w.piece] * p.tau;
+    t_end = min(T, t_beg + p.tau);
   }
 }
 

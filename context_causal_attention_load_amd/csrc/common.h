@@ -55,21 +55,22 @@ __device__ __forceinline__ void dma16_sv(const char* base, unsigned voff, unsign
 constexpr int kNumXcd = 8;
 
 // Decode work placement: a 1-D grid of decode_xcd_blocks(n_inner, hkv, batch) workgroups in
-// which block id -> (inner index, kv head g, sequence b) puts every block of kv head g on XCD
-// g % kNumXcd (id % kNumXcd). The split kernels use it with inner = split and the merge with
-// inner = query head within the group, so a kv head's partials are written and read on one XCD.
-// Blocks past the last kv head (when hkv is not a multiple of kNumXcd) return false.
+// which block id -> (inner index, kv head g, sequence b) puts every block of the pair
+// p = b * hkv + g on XCD p % kNumXcd (id % kNumXcd), the pairs dealt round-robin over the XCDs
+// (with hkv a multiple of kNumXcd that is XCD g % kNumXcd). The split kernels use it with
+// inner = split (and head block) and the merge with inner = query head within the group, so a
+// pair's partials are written and read on one XCD, and every XCD gets work even with fewer kv
+// heads than XCDs. Blocks past the last pair return false.
 inline int64_t decode_xcd_blocks(int n_inner, int hkv, int batch) {
-  return (int64_t)kNumXcd * n_inner * ((hkv + kNumXcd - 1) / kNumXcd) * batch;
+  return (int64_t)kNumXcd * n_inner * (((int64_t)batch * hkv + kNumXcd - 1) / kNumXcd);
 }
 __device__ __forceinline__ bool decode_xcd_item(int id, int n_inner, int hkv, int batch, int& inner, int& g, int& b) {
-  const int xcd = id % kNumXcd, j = id / kNumXcd;  // j enumerates (sequence, kv head / kNumXcd, inner)
+  const int xcd = id % kNumXcd, j = id / kNumXcd;  // j enumerates (pair / kNumXcd, inner)
   inner = j % n_inner;
-  const int t = j / n_inner;
-  const int ng = (hkv + kNumXcd - 1) / kNumXcd;
-  b = t / ng;
-  g = (t % ng) * kNumXcd + xcd;
-  return g < hkv && b < batch;
+  const int pair = (j / n_inner) * kNumXcd + xcd;
+  b = pair / hkv;
+  g = pair % hkv;
+  return b < batch;
 }
 
 // ---- launchers (defined in the .hip files; return the launch status) ----

@@ -11,12 +11,12 @@
 //    to len_b and all G query heads of g; it writes (max, sum, unnormalised output) partials.
 //    Splits past len_b exit at once, so nothing beyond the valid length is ever loaded.
 //  * Second pass: the partials of each (b, h) are merged with log-sum-exp weights.
-//  * bf16, D = 128, G <= 16 (the fast path): every K and V load of the split is issued before
-//    any arithmetic, so a workgroup keeps its whole 2 x 64 KB split in flight; scores use v_dot2
-//    on bf16 pairs with 4 lanes per key row and a DPP reduction. Above 8 heads the heads are
-//    taken in two groups over the same registers.
-//  * Other cases (fp32 caches, D = 64, G > 16) use a simpler split kernel with the same partial
-//    layout.
+//  * bf16, D = 128, G <= 8 (the fast path): every K and V load of the split is issued before any
+//    arithmetic, so a workgroup keeps its whole 2 x 64 KB split in flight; scores use v_dot2
+//    on bf16 pairs with 4 lanes per key row and a DPP reduction.
+//  * bf16, D = 128, G > 8: the products are a dense contraction (each byte feeds G heads) and run
+//    on the matrix cores, in workgroups of up to 16 query heads.
+//  * Other cases (fp32 caches, D = 64) use a simpler split kernel with the same partial layout.
 //  * The merge is a separate launch: merging inside the split kernel (last workgroup to
 //    arrive) needs a device-scope release per workgroup, which on this part writes back the
 //    whole L2 and costs far more than the second launch.
@@ -210,9 +210,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   }
 }
 
-// Block -> (sequence b, query head h) of the merge, with the kv head of h on the XCD where the
-// split kernel ran that kv head's splits (decode_xcd_item), so the partials may still be in
-// that XCD's L2.
+// Block -> (sequence b, query head h) of the merge, on the XCD where the split kernel ran the
+// splits of (b, kv head of h) (decode_xcd_item), so the partials may still be in that XCD's L2.
 __device__ __forceinline__ bool merge_item(const DecParams& p, int& b, int& h) {
   int hg, g;
   if (!decode_xcd_item(blockIdx.x, p.G, p.Hkv, p.B, hg, g, b)) return false;
@@ -376,18 +375,15 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
   constexpr int VS = kFastThreads / LPRV;  // V row slots
   constexpr int VR = SL / VS;              // V rows per lane (consecutive pairs share a v_dot2)
   static_assert(SL % KROWS == 0 && SL % VS == 0 && VR % 2 == 0, "split / thread layout mismatch");
-  // The P V reduction buffer holds HG <= 8 heads; more than 8 query heads per kv head are taken
-  // in NG groups of HG (12 -> 6 + 6, 16 -> 8 + 8) over the same V registers. It shares its LDS
-  // with the scores, which are dead once the probabilities are formed, so 16 heads still fit
-  // three workgroups per CU.
-  constexpr int NG = (G + 7) / 8;
-  constexpr int HG = (G + NG - 1) / NG;
-  constexpr int kRedFloats = kFastWaves * HG * D;
+  // The P V reduction buffer shares its LDS with the scores, which are dead once the
+  // probabilities are formed.
+  static_assert(G <= kFastWaves, "one wave per head in the softmax pass");
+  constexpr int kRedFloats = kFastWaves * G * D;
   constexpr int kScoreFloats = G * SL;
 
   __shared__ float s_sr[kRedFloats > kScoreFloats ? kRedFloats : kScoreFloats];
   float(*s_s)[SL] = reinterpret_cast<float(*)[SL]>(s_sr);           // scores, log2 units
-  float(*s_red)[HG][D] = reinterpret_cast<float(*)[HG][D]>(s_sr);   // per-wave P V sums
+  float(*s_red)[G][D] = reinterpret_cast<float(*)[G][D]>(s_sr);     // per-wave P V sums
   __shared__ __attribute__((aligned(16))) __bf16 s_pb[G][VS][VR];  // bf16 probabilities by V slot
   __shared__ __attribute__((aligned(16))) __bf16 s_q[G][D];
   __shared__ float s_m[G], s_l[G];
@@ -466,7 +462,8 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
   // ---- per-head max / probabilities / sum over the split: one wave per head. Probabilities
   // are rounded to bf16 once; the sum adds the rounded values, and they are stored where the
   // P V step reads them (by V row slot, consecutive rows of a slot adjacent).
-  for (int h = wave; h < G; h += kFastWaves) {
+  if (wave < G) {
+    const int h = wave;
     float x[SL / 64];
     float m = -INFINITY;
 #pragma unroll
@@ -512,54 +509,237 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
   const int rowq = lane / 16;
   const int tsel = (rowq == 0) ? 0 : (rowq == 1 ? 2 : (rowq == 2 ? 1 : 3));
 #pragma unroll
-  for (int grp = 0; grp < NG; ++grp) {
-    const int h0 = grp * HG;                   // first query head of the group
-    const int hn = HG < G - h0 ? HG : G - h0;  // heads in the group
-    if (grp > 0) __syncthreads();              // the previous group's partials are read out
+  for (int h = 0; h < G; ++h) {
+    float a8[8];
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      if (hh < hn) {
-        float a8[8];
+    for (int e = 0; e < 8; ++e) a8[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a8[e] = 0.f;
+    for (int pi = 0; pi < VR / 2; ++pi) {
+      const unsigned pw = reinterpret_cast<const unsigned*>(&s_pb[h][vslot][0])[pi];
 #pragma unroll
-        for (int pi = 0; pi < VR / 2; ++pi) {
-          const unsigned pw = reinterpret_cast<const unsigned*>(&s_pb[h0 + hh][vslot][0])[pi];
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            a8[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw), as_bf16x2(vp[pi][e]), a8[e], false);
-        }
-        float hv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(a8[2 * i]), __float_as_uint(a8[2 * i + 1]), false,
-                                                     false);
-          hv[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(hv[2 * j]), __float_as_uint(hv[2 * j + 1]), false,
-                                                     false);
-          s_red[wave][hh][vc * 8 + 4 * j + tsel] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-        }
-      }
+      for (int e = 0; e < 8; ++e) a8[e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw), as_bf16x2(vp[pi][e]), a8[e], false);
     }
-    __syncthreads();
-
-    // ---- this split's partial: (o[0..D), max, sum) per head of the group
-    for (int idx = tid; idx < hn * D; idx += kFastThreads) {
-      const int hh = idx / D, d = idx % D, h = h0 + hh;
-      float x = 0.f;
+    float hv[4];
 #pragma unroll
-      for (int wv = 0; wv < kFastWaves; ++wv) x += s_red[wv][hh][d];
-      float* part = p.ws + (((int64_t)b * p.Hq + g * p.G + h) * p.nsplit + split) * (D + 2);
-      part[d] = x;
-      if (d == 0) {
-        part[D] = s_m[h];
-        part[D + 1] = s_l[h];
-      }
+    for (int i = 0; i < 4; ++i) {
+      auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(a8[2 * i]), __float_as_uint(a8[2 * i + 1]), false,
+                                                 false);
+      hv[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(hv[2 * j]), __float_as_uint(hv[2 * j + 1]), false,
+                                                 false);
+      s_red[wave][h][vc * 8 + 4 * j + tsel] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
     }
   }
+  __syncthreads();
+
+  // ---- this split's partial: (o[0..D), max, sum) per head
+  for (int idx = tid; idx < G * D; idx += kFastThreads) {
+    const int h = idx / D, d = idx % D;
+    float x = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kFastWaves; ++wv) x += s_red[wv][h][d];
+    float* part = p.ws + (((int64_t)b * p.Hq + g * p.G + h) * p.nsplit + split) * (D + 2);
+    part[d] = x;
+    if (d == 0) {
+      part[D] = s_m[h];
+      part[D + 1] = s_l[h];
+    }
+  }
+}
+
+// ---- bf16, D = 128, G > 8: both products on the matrix cores ----
+// With more than 8 query heads per kv head every cached byte feeds that many heads, and the
+// products are a dense contraction the v_dot2 path can no longer hide under the reads (its time
+// grows with G: 39 us at G = 6, 56 us at 12, 64 us at 16 on the 24 x 8 x 2048 cache, against
+// 40 and 41 us here at 12 and 16). There the two products run on v_mfma_f32_16x16x32_bf16, as
+// in the int8 decode: workgroup = (block of up to 16 query heads, 256-key split, kv head, sequence), 4 waves
+// of 64 keys. The head blocks of one split are dispatched next to each other on one XCD, so the
+// second reads the split's K and V from that XCD's L2.
+//  * S^T = K Q^T per 16-key block: lane (key col, group gq) holds dims 32 gq + 8 i .. + 7 of its
+//    key row for k-step i (the same permutation in Q), 64 contiguous bytes per lane and block.
+//  * O^T = V^T P^T per 32-key block and 16-dim block, P in registers as the B operand. The
+//    wave's V rows reach LDS by direct-to-LDS copies with XOR-swizzled 16-byte chunks and come
+//    back through the transposing read ds_read_b64_tr_b16 (a 16-lane group reads 4 rows x 16
+//    dims; output lane j holds dim j of the 4 rows), two reads per MFMA.
+//  * The max is taken over the whole workgroup, so the waves' partials add without rescaling;
+//    the partial layout is the other split kernels', and the same merge finishes the call.
+constexpr int kMfThreads = 256;
+constexpr int kMfWaves = kMfThreads / 64;
+constexpr int kMfHeads = 16;                                  // query heads per workgroup (MFMA N)
+constexpr int kMfD = 128;
+constexpr int kMfRowBytes = kMfD * 2;
+constexpr int kMfOStride = kMfD + 4;                           // fp32 stride of the wave outputs
+constexpr int kMfVBytes = kDecodeSplitLen * kMfRowBytes;       // 64 KB V tile
+constexpr int kMfOBytes = kMfWaves * kMfHeads * kMfOStride * 4;
+constexpr int kMfLdsBytes = kMfVBytes > kMfOBytes ? kMfVBytes : kMfOBytes;
+static_assert(kDecodeSplitLen == kMfWaves * 64, "a wave owns 64 keys of the split");
+
+// Slot of the V tile's 16-byte chunk c of row r: c ^ mf_swz(r). The 4 rows one 16-lane group
+// reads in a transposed load (r & 3 = 0..3) land in 4 distinct 32-byte slots.
+__device__ __forceinline__ int mf_swz(int r) { return (2 * (r & 3)) ^ (8 * ((r >> 2) & 1)); }
+
+__global__ __launch_bounds__(kMfThreads) void decode_bf16_mfma_split_kernel(DecParams p, int nhb) {
+  constexpr int SL = kDecodeSplitLen;
+  constexpr int D = kMfD;
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  __shared__ __attribute__((aligned(16))) char s_v[kMfLdsBytes];  // V tile, then the wave outputs
+  __shared__ float s_max[kMfWaves][kMfHeads];
+  __shared__ float s_sum[kMfWaves][kMfHeads];
+
+  int inner, g, b;  // the (b, g) pair's XCD, as in the merge that reads the partials
+  if (!decode_xcd_item(blockIdx.x, p.nsplit * nhb, p.Hkv, p.B, inner, g, b)) return;
+  const int hb = inner % nhb, split = inner / nhb;
+  int len = p.lengths[b];
+  len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+  const int k0 = split * SL;
+  if (k0 >= len) return;
+  const int nk = min(SL, len - k0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, gq = lane >> 4;
+
+  const int64_t row0 = ((int64_t)b * p.Hkv + g) * p.max_len + k0;  // cache row of the split's key 0
+  const char* kt = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.k) + row0 * D);
+  const char* vt = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.v) + row0 * D);
+
+  // Every load of the split is issued before the first wait, V first (the V copies go straight
+  // to LDS through inline asm, which the compiler does not count; loads return in order, so
+  // each wait the compiler places for its own loads also covers them). No load sits in a
+  // branch; rows past the valid length re-read the last valid row (finite, masked).
+  // ---- V rows of this wave into LDS: copy u moves rows 64 wave + 4 u .. + 3 (1 KB); lane l
+  // fills slot l & 15 of row l >> 4 with the chunk the swizzle puts there.
+  const unsigned lds_v = (unsigned)(uintptr_t)s_v;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int r = wave * 64 + u * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ mf_swz(r);
+    dma16_sv(vt, (unsigned)(min(r, nk - 1) * kMfRowBytes + c * 16), lds_v + (wave * 64 + u * 4) * kMfRowBytes);
+  }
+  // ---- K: key block kb of this wave, row col, bytes [64 gq, 64 gq + 64)
+  u32x4 kr[4][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int row = min(wave * 64 + kb * 16 + col, nk - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(kt + (int64_t)row * kMfRowBytes + 64 * gq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kr[kb][i] = src[i];
+  }
+  // ---- queries (B operand): head col of the block, dims 32 gq + 8 i .. + 7 for k-step i; a
+  // column past the group's last head reads that head and is then zeroed
+  const int hg = hb * kMfHeads + col;  // head within the group
+  const bool hvalid = hg < p.G;
+  bf16x8 qf[4];
+  {
+    const __bf16* qh = static_cast<const __bf16*>(p.q) + ((int64_t)b * p.Hq + (int64_t)g * p.G + min(hg, p.G - 1)) * D +
+                       32 * gq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(qh + 8 * i);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qf[i] = __builtin_bit_cast(bf16x8, hvalid ? raw : z);
+    }
+  }
+
+  // ---- scores (log2 units): lane holds head col, keys 64 wave + 16 kb + 4 gq + j
+  float x[4][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kb][i]), qf[i], acc, 0, 0, 0);
+    const int key0 = wave * 64 + kb * 16 + 4 * gq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[kb][j] = key0 + j < nk ? acc[j] * p.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[kb][j]);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (lane < 16) s_max[wave][lane] = mx;
+  __syncthreads();
+  float M = s_max[0][col];
+#pragma unroll
+  for (int w = 1; w < kMfWaves; ++w) M = fmaxf(M, s_max[w][col]);  // finite: key 0 is valid
+
+  // ---- probabilities: rounded to bf16 once; the sum adds the rounded values
+  float l = 0.f;
+  __bf16 pv[4][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pv[kb][j] = (__bf16)__builtin_amdgcn_exp2f(x[kb][j] - M);
+      l += (float)pv[kb][j];
+    }
+  }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  // ---- O^T += V^T P^T. Group gq's transposed reads for key block t: lane 4e + q of the group
+  // reads row 64 wave + 32 t + 4 gq + e (lo) or that + 16 (hi), dims 16 db + 4 q .. + 3; the 8
+  // keys are those of pv[2t][0..3], pv[2t + 1][0..3] in that order.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's V copies have landed
+  const int e = (lane & 15) >> 2, q4 = lane & 3;
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const bf16x8 pb8 = {pv[2 * t][0], pv[2 * t][1], pv[2 * t][2], pv[2 * t][3],
+                        pv[2 * t + 1][0], pv[2 * t + 1][1], pv[2 * t + 1][2], pv[2 * t + 1][3]};
+    const int rlo = wave * 64 + 32 * t + 4 * gq + e, rhi = rlo + 16;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const int c = 2 * db + (q4 >> 1), within = 8 * (q4 & 1);
+      const char* alo = s_v + rlo * kMfRowBytes + ((c ^ mf_swz(rlo)) * 16) + within;
+      const char* ahi = s_v + rhi * kMfRowBytes + ((c ^ mf_swz(rhi)) * 16) + within;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(alo));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(ahi));
+      const i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cat), pb8, oacc[db], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave's transposed reads are done: the tile memory takes the outputs
+
+  // ---- sum of the four waves' outputs: lane holds head col, dims 16 db + 4 gq + r
+  float* s_o = reinterpret_cast<float*>(s_v);
+  if (hvalid) {
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      *reinterpret_cast<f32x4*>(&s_o[(wave * kMfHeads + col) * kMfOStride + 16 * db + 4 * gq]) = oacc[db];
+  }
+  if (lane < 16) s_sum[wave][lane] = l;
+  __syncthreads();
+  const int nh = min(kMfHeads, p.G - hb * kMfHeads);
+  for (int idx = tid; idx < nh * D; idx += kMfThreads) {
+    const int h = idx / D, d = idx % D;
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMfWaves; ++w) o += s_o[(w * kMfHeads + h) * kMfOStride + d];
+    float* part = p.ws + (((int64_t)b * p.Hq + (int64_t)g * p.G + hb * kMfHeads + h) * p.nsplit + split) * (D + 2);
+    part[d] = o;
+    if (d == 0) {
+      float m = s_max[0][h], s = s_sum[0][h];
+#pragma unroll
+      for (int w = 1; w < kMfWaves; ++w) m = fmaxf(m, s_max[w][h]);
+#pragma unroll
+      for (int w = 1; w < kMfWaves; ++w) s += s_sum[w][h];
+      part[D] = m;
+      part[D + 1] = s;
+    }
+  }
+}
+
+void launch_mfma_128(const DecParams& p, hipStream_t stream) {
+  const int nhb = (p.G + kMfHeads - 1) / kMfHeads;
+  hipLaunchKernelGGL(decode_bf16_mfma_split_kernel, dim3(decode_xcd_blocks(p.nsplit * nhb, p.Hkv, p.B)),
+                     dim3(kMfThreads), 0, stream, p, nhb);
 }
 
 template <int D, int G>
@@ -578,14 +758,6 @@ bool launch_fast_128(const DecParams& p, hipStream_t stream) {
     case 6: launch_fast<128, 6>(p, stream); return true;
     case 7: launch_fast<128, 7>(p, stream); return true;
     case 8: launch_fast<128, 8>(p, stream); return true;
-    case 9: launch_fast<128, 9>(p, stream); return true;
-    case 10: launch_fast<128, 10>(p, stream); return true;
-    case 11: launch_fast<128, 11>(p, stream); return true;
-    case 12: launch_fast<128, 12>(p, stream); return true;
-    case 13: launch_fast<128, 13>(p, stream); return true;
-    case 14: launch_fast<128, 14>(p, stream); return true;
-    case 15: launch_fast<128, 15>(p, stream); return true;
-    case 16: launch_fast<128, 16>(p, stream); return true;
     default: return false;
   }
 }
@@ -611,6 +783,11 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   if (p.B == 0 || p.Hq == 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
     if (a.d == 128 && launch_fast_128(p, stream)) {
+      launch_merge<T, 128>(p, stream);
+      return hipGetLastError();
+    }
+    if (a.d == 128) {  // G > 8
+      launch_mfma_128(p, stream);
       launch_merge<T, 128>(p, stream);
       return hipGetLastError();
     }

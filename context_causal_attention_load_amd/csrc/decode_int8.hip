@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kI8Threads) void decode_i8_split_kernel(I8Params p)
   __shared__ float s_max[kI8Waves][kHeadBlock];
   __shared__ float s_sum[kI8Waves][kHeadBlock];
 
-  int inner, g, b;  // kv head g on XCD g % kNumXcd, as in the merge that reads the partials
+  int inner, g, b;  // the (b, g) pair's XCD, as in the merge that reads the partials
   if (!decode_xcd_item(blockIdx.x, p.nsplit * p.nhb, p.Hkv, p.B, inner, g, b)) return;
   const int split = inner % p.nsplit, hb = inner / p.nsplit;
   int len = p.lengths[b];

@@ -355,7 +355,11 @@ def test_decode_full_workload_with_poisoned_tail():
     (2, 9, 1, 128, 513, torch.bfloat16, [513, 257]),          # G=9: P V groups of 5 and 4
     (3, 24, 2, 128, 800, torch.bfloat16, [800, 1, 256]),      # G=12: groups of 6 and 6
     (2, 26, 2, 128, 600, torch.bfloat16, [600, 299]),         # G=13: groups of 7 and 6
-    (2, 17, 1, 128, 300, torch.bfloat16, [300, 45]),          # G=17: the generic kernel
+    (2, 17, 1, 128, 300, torch.bfloat16, [300, 45]),          # G=17: matrix-core kernel, blocks of 16 + 1
+    (2, 32, 1, 128, 1000, torch.bfloat16, [1000, 513]),       # G=32: two full head blocks
+    (3, 96, 2, 128, 700, torch.bfloat16, [700, 1, 257]),      # G=48, two kv heads
+    (2, 20, 1, 128, 64, torch.float32, [64, 33]),             # fp32, G=20: the generic kernel
+    (5, 160, 5, 128, 900, torch.bfloat16, [900, 1, 256, 257, 613]),  # 25 (sequence, kv head) pairs
     (2, 8, 8, 64, 513, torch.float32, [513, 17]),
     (5, 12, 4, 64, 1000, torch.bfloat16, [999, 1000, 512, 3, 768]),
     (2, 4, 2, 128, 64, torch.float32, [64, 33]),

@@ -11,12 +11,13 @@
 //    to len_b and all G query heads of g; it writes (max, sum, unnormalised output) partials.
 //    Splits past len_b exit at once, so nothing beyond the valid length is ever loaded.
 //  * Second pass: the partials of each (b, h) are merged with log-sum-exp weights.
-//  * bf16, D = 128, G <= 8 (the fast path): every K and V load of the split is issued before any
-//    arithmetic, so a workgroup keeps its whole 2 x 64 KB split in flight; scores use v_dot2
-//    on bf16 pairs with 4 lanes per key row and a DPP reduction.
+//  * bf16, D = 128 or 64, G <= 8 (the fast path): every K and V load of the split is issued
+//    before any arithmetic, so a workgroup keeps its whole split (2 x 64 KB at D = 128) in
+//    flight; scores use v_dot2 on bf16 pairs with 4 lanes per key row and a DPP reduction.
 //  * bf16, D = 128, G > 8: the products are a dense contraction (each byte feeds G heads) and run
 //    on the matrix cores, in workgroups of up to 16 query heads.
-//  * Other cases (fp32 caches, D = 64) use a simpler split kernel with the same partial layout.
+//  * Other cases (fp32 caches, D = 64 with G > 8) use a simpler split kernel with the same
+//    partial layout.
 //  * The merge is a separate launch: merging inside the split kernel (last workgroup to
 //    arrive) needs a device-scope release per workgroup, which on this part writes back the
 //    whole L2 and costs far more than the second launch.
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
   // ---- unnormalised P V: v_dot2 over pairs of this lane's rows (p pair . v pair per dim).
   // The (row a, row b) bf16 pairs of every dim are formed once; heads are then done one at a
   // time so only 8 accumulators are live.
-  static_assert(LPRV == 16, "the slot reduction below assumes 16 lanes per V row");
+  static_assert(LPRV == 16 || LPRV == 8, "the slot reduction below takes 16 or 8 lanes per V row");
   unsigned vp[VR / 2][8];
 #pragma unroll
   for (int pi = 0; pi < VR / 2; ++pi) {
@@ -502,12 +503,12 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
       vp[pi][2 * j + 1] = __builtin_amdgcn_perm(c, a, 0x07060302u);  // dim 2j+1 of rows (a, b)
     }
   }
-  // Sum over the 4 row slots of the wave with lane-swap "transpose" steps, each reducing two
-  // accumulators: after the 32-lane step the lower half of register i holds dim 2i and the upper
-  // half dim 2i+1; after the 16-lane step each 16-lane row of register j holds one of dims
-  // 4j..4j+3 (rows 0..3 -> 4j, 4j+2, 4j+1, 4j+3).
-  const int rowq = lane / 16;
-  const int tsel = (rowq == 0) ? 0 : (rowq == 1 ? 2 : (rowq == 2 ? 1 : 3));
+  // Sum over the row slots of the wave (4 of 16 lanes at D = 128, 8 of 8 lanes at D = 64) with
+  // lane-swap "transpose" steps, each reducing two accumulators: after the 32-lane step the
+  // lower half of register i holds dim 2i and the upper half dim 2i+1 (H = lane bit 5); after
+  // the 16-lane step row R (lane bit 4) of register j holds dim 4j + 2R + H; at D = 64 a third
+  // step between lanes 8 apart (S = lane bit 3) leaves dim 4S + 2R + H of the lane's chunk.
+  const int hsel = ((lane >> 4) & 1) * 2 + (lane >> 5);  // 2R + H
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float a8[8];
@@ -526,11 +527,22 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
                                                  false);
       hv[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
     }
+    float h2[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(hv[2 * j]), __float_as_uint(hv[2 * j + 1]), false,
                                                  false);
-      s_red[wave][h][vc * 8 + 4 * j + tsel] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+      h2[j] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    }
+    if constexpr (LPRV == 16) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) s_red[wave][h][vc * 8 + 4 * j + hsel] = h2[j];
+    } else {
+      // lanes l and l ^ 8 (a 16-lane row rotated by 8): each keeps h2[S] and adds the other's
+      const bool s_hi = (lane >> 3) & 1;
+      const float send = s_hi ? h2[0] : h2[1], keep = s_hi ? h2[1] : h2[0];
+      const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0x128, 0xF, 0xF, true));
+      s_red[wave][h][vc * 8 + 4 * (int)s_hi + hsel] = keep + got;
     }
   }
   __syncthreads();
@@ -762,6 +774,20 @@ bool launch_fast_128(const DecParams& p, hipStream_t stream) {
   }
 }
 
+bool launch_fast_64(const DecParams& p, hipStream_t stream) {
+  switch (p.G) {
+    case 1: launch_fast<64, 1>(p, stream); return true;
+    case 2: launch_fast<64, 2>(p, stream); return true;
+    case 3: launch_fast<64, 3>(p, stream); return true;
+    case 4: launch_fast<64, 4>(p, stream); return true;
+    case 5: launch_fast<64, 5>(p, stream); return true;
+    case 6: launch_fast<64, 6>(p, stream); return true;
+    case 7: launch_fast<64, 7>(p, stream); return true;
+    case 8: launch_fast<64, 8>(p, stream); return true;
+    default: return false;
+  }
+}
+
 template <typename T>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   DecParams p;
@@ -789,6 +815,10 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     if (a.d == 128) {  // G > 8
       launch_mfma_128(p, stream);
       launch_merge<T, 128>(p, stream);
+      return hipGetLastError();
+    }
+    if (a.d == 64 && launch_fast_64(p, stream)) {
+      launch_merge<T, 64>(p, stream);
       return hipGetLastError();
     }
   }

@@ -360,6 +360,8 @@ def test_decode_full_workload_with_poisoned_tail():
     (3, 96, 2, 128, 700, torch.bfloat16, [700, 1, 257]),      # G=48, two kv heads
     (2, 20, 1, 128, 64, torch.float32, [64, 33]),             # fp32, G=20: the generic kernel
     (5, 160, 5, 128, 900, torch.bfloat16, [900, 1, 256, 257, 613]),  # 25 (sequence, kv head) pairs
+    (3, 32, 4, 64, 2048, torch.bfloat16, [2048, 1, 1500]),    # D=64, G=8: 8 lanes per V row
+    (3, 24, 2, 64, 300, torch.bfloat16, [300, 17, 256]),      # D=64, G=12: the generic kernel
     (2, 8, 8, 64, 513, torch.float32, [513, 17]),
     (5, 12, 4, 64, 1000, torch.bfloat16, [999, 1000, 512, 3, 768]),
     (2, 4, 2, 128, 64, torch.float32, [64, 33]),
@@ -391,6 +393,22 @@ def test_decode_llama405b_shape():
     scale = 1.0 / math.sqrt(128)
     O_ref, L_ref = oatt.decode_ref(q, kc, vc, lengths.numpy(), scale)
     for b in range(8):
+        kc[b, :, lengths[b]:] = float("nan")
+        vc[b, :, lengths[b]:] = float("nan")
+    o, lse = run_decode(lengths, q, kc, vc, scale)
+    assert_close(o, O_ref, 2e-2, "decode O")
+    assert_close(lse, L_ref, 2e-2, "decode LSE")
+
+
+def test_decode_llama32_1b_shape():
+    """Llama3.2-1B-shaped decode (32 query heads over 8 kv heads, head dim 64) over 16
+    sequences of mixed length up to 4096, NaN past every length."""
+    announce("decode Llama3.2-1B shape: B=16, Hq=32, Hkv=8, D=64, Lmax=4096")
+    lengths, q, kc, vc = synth.decode_inputs(16, 32, 8, 64, 4096, 1, 4096, torch.bfloat16, seed=321)
+    lengths[3] = 4096
+    scale = 1.0 / math.sqrt(64)
+    O_ref, L_ref = oatt.decode_ref(q, kc, vc, lengths.numpy(), scale)
+    for b in range(16):
         kc[b, :, lengths[b]:] = float("nan")
         vc[b, :, lengths[b]:] = float("nan")
     o, lse = run_decode(lengths, q, kc, vc, scale)

@@ -102,9 +102,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(FwdParams p, BwdExtra e)
 // ------------------------------------------------------------------------------------------
 // dq kernel
 // ------------------------------------------------------------------------------------------
+constexpr int kDqTileKeys = 64;  // keys per K/V tile of the dq kernel
+
 template <int DQK, int DV>
 struct DqCfg {
-  static constexpr int BK = 64;
+  static constexpr int BK = kDqTileKeys;
   static constexpr int KCH = DQK / 8;
   static constexpr int VCH = DV / 8;
   static constexpr int K_BYTES = BK * KCH * 16;
@@ -374,11 +376,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
 // slot of the caller's workspace, and this kernel adds a cut row block's slots in piece order
 // (a fixed order, so the result does not depend on timing).
 // ------------------------------------------------------------------------------------------
-constexpr int kDqSplitMinTiles = 16;  // no piece below 1024 keys (64-key tiles)
+constexpr int kDqSplitMinTiles = 1024 / kDqTileKeys;  // no piece below 1024 keys
 
 bool plan_dq_split(const AttnBwdArgs& a, const FwdParams& p, SplitPlan& sp) {
   if (a.q_pos) return false;
-  return plan_split_tiles(p, 64, kDqSplitMinTiles, sp);
+  return plan_split_tiles(p, kDqTileKeys, kDqSplitMinTiles, sp);
+}
+
+// The forward's work decomposition of the backward's shape (the dq kernel walks it).
+FwdParams bwd_work_params(const AttnBwdArgs& a) {
+  AttnArgs fa{};
+  fa.q = a.q;
+  fa.k = a.k;
+  fa.v = a.v;
+  fa.q_pos = a.q_pos;
+  fa.batch = a.batch;
+  fa.seq = a.seq;
+  fa.sq = a.sq;
+  fa.hq = a.hq;
+  fa.hkv = a.hkv;
+  fa.d_qk = a.d_qk;
+  fa.d_v = a.d_v;
+  fa.cp = a.cp;
+  fa.rank = a.rank;
+  fa.scale = a.scale;
+  return make_params(fa);
 }
 
 struct DqMergeParams {
@@ -902,24 +924,7 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
 
 template <int DQK, int DV>
 hipError_t launch_bwd_typed(const AttnBwdArgs& a, hipStream_t stream) {
-  AttnArgs fa;
-  fa.q = a.q;
-  fa.k = a.k;
-  fa.v = a.v;
-  fa.q_pos = a.q_pos;
-  fa.o = nullptr;
-  fa.lse = nullptr;
-  fa.batch = a.batch;
-  fa.seq = a.seq;
-  fa.sq = a.sq;
-  fa.hq = a.hq;
-  fa.hkv = a.hkv;
-  fa.d_qk = DQK;
-  fa.d_v = DV;
-  fa.cp = a.cp;
-  fa.rank = a.rank;
-  fa.scale = a.scale;
-  const FwdParams p = make_params(fa);
+  const FwdParams p = bwd_work_params(a);
 
   BwdExtra e;
   e.o = static_cast<const __bf16*>(a.o);
@@ -1008,19 +1013,7 @@ size_t attn_bwd_workspace_bytes(int batch, int sq, int hq) {
 }
 
 size_t attn_bwd_split_workspace_bytes(const AttnBwdArgs& a) {
-  AttnArgs fa{};
-  fa.q_pos = a.q_pos;
-  fa.batch = a.batch;
-  fa.seq = a.seq;
-  fa.sq = a.sq;
-  fa.hq = a.hq;
-  fa.hkv = a.hkv;
-  fa.d_qk = a.d_qk;
-  fa.d_v = a.d_v;
-  fa.cp = a.cp;
-  fa.rank = a.rank;
-  fa.scale = a.scale;
-  const FwdParams p = make_params(fa);
+  const FwdParams p = bwd_work_params(a);
   SplitPlan sp;
   const size_t base = attn_bwd_workspace_bytes(a.batch, a.sq, a.hq);
   if (p.n_items == 0 || !plan_dq_split(a, p, sp)) return base;

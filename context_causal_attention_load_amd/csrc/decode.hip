@@ -564,10 +564,10 @@ __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecP
 
 // ---- bf16, D = 128, G > 8: both products on the matrix cores ----
 // With more than 8 query heads per kv head every cached byte feeds that many heads, and the
-// products are a dense contraction the v_dot2 path can no longer hide under the reads (its time
-// grows with G: 39 us at G = 6, 56 us at 12, 64 us at 16 on the 24 x 8 x 2048 cache, against
-// 40 and 41 us here at 12 and 16). There the two products run on v_mfma_f32_16x16x32_bf16, as
-// in the int8 decode: workgroup = (block of up to 16 query heads, 256-key split, kv head, sequence), 4 waves
+// products are a dense contraction the v_dot2 kernel can no longer hide under the reads (taking
+// the heads in groups of at most 8 over the same registers, it ran 56 us at G = 12 and 64 us at
+// G = 16 on the 24 x 8 x 2048 cache, against 39 us at G = 6 and 40 and 41 us here). There the
+// two products run on v_mfma_f32_16x16x32_bf16, as in the int8 decode: workgroup = (block of up to 16 query heads, 256-key split, kv head, sequence), 4 waves
 // of 64 keys. The head blocks of one split are dispatched next to each other on one XCD, so the
 // second reads the split's K and V from that XCD's L2.
 //  * S^T = K Q^T per 16-key block: lane (key col, group gq) holds dims 32 gq + 8 i .. + 7 of its

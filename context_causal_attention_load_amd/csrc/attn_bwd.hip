@@ -21,8 +21,8 @@
 //  * dkdv: key-stationary. A workgroup owns 32 keys per wave of one kv head (256 keys at
 //    Dqk = 128, else 128); the keys' K' (scaled) and V fragments stay in registers as B operands.
 //    It streams (32-row query block, query head) stages of Q, dO, log2-LSE, D and positions
-//    through an LDS ring (3 slots; at Dqk = 192, where a wave has its SIMD to itself, 6 slots
-//    and two stages per barrier), skipping blocks whose rows are all before the keys.
+//    through an LDS ring of 3 slots, skipping blocks whose rows are all before the keys. (At
+//    Dqk = 192 a variant with 16 keys per wave on 16x16x32 MFMAs keeps two waves per SIMD.)
 //    Per stage: S = Q K'^T seeded with
 //    -LSE, dP - D = dO V^T seeded with -D; P and dS come out with a lane per key, already in
 //    the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS, whose A operands are the
@@ -448,13 +448,14 @@ constexpr int kKvStages = 3;  // LDS ring: a stage's copy is issued two stages a
 // Waves per workgroup of the dkdv kernel, 32 keys each. Every workgroup streams the Q and dO rows
 // that see its keys, so more keys per workgroup means fewer passes over that stream: 8 waves
 // (256 keys, one workgroup per CU) at Dqk = 128; 4 at Dqk = 64 (a stage is only four waves' worth
-// of copies) and at Dqk = 192 (one wave per SIMD holds its 342 registers).
+// of copies). Dqk = 192 has its own kernel (16 keys per wave, below).
 template <int DQK>
 struct KvShape {
+  static_assert(DQK <= 128, "Dqk = 192 runs attn_bwd_dkdv16_kernel");
   static constexpr int WAVES = DQK == 128 ? 8 : 4;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int BKV = WAVES * 32;  // keys per workgroup
-  static constexpr int MIN_WG_PER_CU = (WAVES == 8 || DQK > 128) ? 1 : 2;
+  static constexpr int MIN_WG_PER_CU = WAVES == 8 ? 1 : 2;
 };
 
 template <int DQK, int DV>
@@ -474,10 +475,6 @@ struct DkvCfg {
   static constexpr int DV_STEPS = DV / 16;
   static constexpr int MK = DQK / 32;
   static constexpr int MV = DV / 32;
-  // Dqk > 128: one wave per SIMD, so nothing covers a wave's own waits. It then takes two stages
-  // per barrier (see the pair loop), through a ring of three pairs.
-  static constexpr bool PAIR = DQK > 128;
-  static constexpr int RING = PAIR ? 6 : kKvStages;
 };
 
 struct DkvParams {
@@ -497,12 +494,11 @@ __device__ __forceinline__ int load_uniform_i32(const int* ptr) {
   return v;
 }
 
-// One dkdv stage in three steps (the pair loop orders them across two stages).
+// One dkdv stage in three steps.
 // Step 1: S = Q K'^T - LSE and dP - D = dO V^T - D for the stage in LDS at qt (its Q tile, then
-// its dO tile, then log2-LSE, D and positions of its 32 rows).
-// With SCHED, S and dP k-steps alternate and each row-fragment read is kept two MFMAs ahead of
-// its use (the single-stage loop); without, the compiler orders both stages of a pair.
-template <int DQK, int DV, bool SCHED>
+// its dO tile, then log2-LSE, D and positions of its 32 rows). S and dP k-steps alternate and
+// each row-fragment read is kept two MFMAs ahead of its use.
+template <int DQK, int DV>
 __device__ __forceinline__ void dkdv_scores(const char* qt, const bf16x8 (&kf)[DQK / 16], const bf16x8 (&vf)[DV / 16],
                                             f32x16& sacc, f32x16& dacc) {
   using C = DkvCfg<DQK, DV>;
@@ -526,33 +522,20 @@ __device__ __forceinline__ void dkdv_scores(const char* qt, const bf16x8 (&kf)[D
   const char* orow = ot + row * (C::OCH * 16);
   // chunk (2 ks + hl) ^ sw = 2 ks ^ (hl ^ sw): one xor per k-step on a per-lane constant
   const unsigned tq = (unsigned)(lhl ^ swz<C::QCH>(row)), to = (unsigned)(lhl ^ swz<C::OCH>(row));
-  if constexpr (SCHED) {
 #pragma unroll
-    for (int ks = 0; ks < (C::QK_STEPS > C::DV_STEPS ? C::QK_STEPS : C::DV_STEPS); ++ks) {
-      if (ks < C::QK_STEPS) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + ((tq ^ (2u * ks)) << 4));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
-      }
-      if (ks < C::DV_STEPS) {
-        // with equal row layouts the dO tile's offsets are the Q tile's plus its size
-        const bf16x8 a = C::QCH == C::OCH ? *reinterpret_cast<const bf16x8*>(qr + ((tq ^ (2u * ks)) << 4) + C::Q_BYTES)
-                                          : *reinterpret_cast<const bf16x8*>(orow + ((to ^ (2u * ks)) << 4));
-        dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dacc, 0, 0, 0);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < C::QK_STEPS; ++ks) {
+  for (int ks = 0; ks < (C::QK_STEPS > C::DV_STEPS ? C::QK_STEPS : C::DV_STEPS); ++ks) {
+    if (ks < C::QK_STEPS) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(qr + ((tq ^ (2u * ks)) << 4));
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
     }
-#pragma unroll
-    for (int ks = 0; ks < C::DV_STEPS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + ((to ^ (2u * ks)) << 4));
+    if (ks < C::DV_STEPS) {
+      // with equal row layouts the dO tile's offsets are the Q tile's plus its size
+      const bf16x8 a = C::QCH == C::OCH ? *reinterpret_cast<const bf16x8*>(qr + ((tq ^ (2u * ks)) << 4) + C::Q_BYTES)
+                                        : *reinterpret_cast<const bf16x8*>(orow + ((to ^ (2u * ks)) << 4));
       dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], dacc, 0, 0, 0);
     }
   }
-  if constexpr (SCHED) {
+  {
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int i = 0; i < C::QK_STEPS + C::DV_STEPS - 2; ++i) {
@@ -589,7 +572,7 @@ __device__ __forceinline__ void dkdv_probs(const char* qt, bool need_mask, int k
 }
 
 // Step 3: dV^T += dO^T P and dK^T += Q^T dS, A operands from transposing reads of the tiles.
-template <int DQK, int DV, bool SCHED>
+template <int DQK, int DV>
 __device__ __forceinline__ void dkdv_grads(const char* qt, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2],
                                            f32x16 (&dkacc)[DQK / 32], f32x16 (&dvacc)[DV / 32]) {
   using C = DkvCfg<DQK, DV>;
@@ -626,7 +609,7 @@ __device__ __forceinline__ void dkdv_grads(const char* qt, const bf16x8 (&pb)[2]
       dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), dsb[ks], dkacc[m], 0, 0, 0);
     }
   }
-  if constexpr (SCHED) {
+  {
     // keep the transposing reads (two per MFMA) ahead of their MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -642,7 +625,7 @@ template <int DQK, int DV>
 __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU) void attn_bwd_dkdv_kernel(
     DkvParams p, BwdExtra e) {
   using C = DkvCfg<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) char lds[C::RING * C::STAGE];
+  __shared__ __attribute__((aligned(16))) char lds[kKvStages * C::STAGE];
 
   // work item: (b, g, chunk i, tile t). Each XCD takes a contiguous range of items, in which
   // tiles and chunks vary fastest, so an XCD holds whole kv heads (equal work) and its L2 serves
@@ -764,92 +747,6 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
       sqb = prev_visible(sqb - 1);
     }
   };
-  if constexpr (C::PAIR) {
-    // Two stages per barrier: the pair (A, B) is in LDS while the next pair's copies land and
-    // the one after is issued into the slots of the previous pair (six slots, three pairs).
-    // Within the pair the steps run as S(A); probs(A) with S(B); grads(A) with probs(B);
-    // grads(B), so that one stage's softmax overlaps the other stage's matrix products.
-    int sq[4], sh[4];  // stages A, B (in LDS) and C, D (in flight); qb < 0: none
-    sq[0] = prev_visible(e.nqb - 1);
-    sh[0] = 0;
-#pragma unroll
-    for (int i = 1; i < 4; ++i) {
-      sq[i] = sq[i - 1];
-      sh[i] = sh[i - 1];
-      advance(sq[i], sh[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (sq[i] >= 0) dma_stage(sq[i], g * p.G + sh[i], i);
-    // A and B must have landed; C and D may stay in flight
-    if (sq[3] >= 0) {
-      if (wave < 3)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (C::Q_DMA + C::O_DMA + 1)) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (C::Q_DMA + C::O_DMA)) : "memory");
-    } else if (sq[2] >= 0) {
-      if (wave < 3)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA + 1) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();
-    int slot = 0;  // ring slot of A; B is slot + 1
-    while (sq[0] >= 0) {
-      int eq = sq[3], eh = sh[3];
-      advance(eq, eh);
-      int fq = eq, fh = eh;
-      advance(fq, fh);
-      const int se = slot + 4 >= C::RING ? slot + 4 - C::RING : slot + 4;  // the previous pair's slots
-      if (eq >= 0) dma_stage(eq, g * p.G + eh, se);
-      if (fq >= 0) dma_stage(fq, g * p.G + fh, se + 1);
-
-      const char* qa = lds + slot * C::STAGE;
-      const char* qb_t = qa + C::STAGE;
-      const bool has_b = sq[1] >= 0;
-      const bool mask_a = load_uniform_i32(blkmin + sq[0]) < kpos0 + C::BKV - 1 || nvalid < C::BKV ||
-                          (sq[0] + 1) * kBQ > p.Sq;
-      const bool mask_b = has_b && (load_uniform_i32(blkmin + sq[1]) < kpos0 + C::BKV - 1 || nvalid < C::BKV ||
-                                    (sq[1] + 1) * kBQ > p.Sq);
-      f32x16 sa, da, sb, db;
-      bf16x8 pba[2], dsa[2], pbb[2], dsbb[2];
-      dkdv_scores<DQK, DV, false>(qa, kf, vf, sa, da);
-      dkdv_probs<DQK, DV>(qa, mask_a, kk, kpos, nvalid, sa, da, pba, dsa);
-      if (has_b) dkdv_scores<DQK, DV, false>(qb_t, kf, vf, sb, db);
-      dkdv_grads<DQK, DV, false>(qa, pba, dsa, dkacc, dvacc);
-      if (has_b) {
-        dkdv_probs<DQK, DV>(qb_t, mask_b, kk, kpos, nvalid, sb, db, pbb, dsbb);
-        dkdv_grads<DQK, DV, false>(qb_t, pbb, dsbb, dkacc, dvacc);
-      }
-
-      // the next pair's copies must have landed; the pair after may stay in flight
-      if (fq >= 0) {
-        if (wave < 3)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (C::Q_DMA + C::O_DMA + 1)) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (C::Q_DMA + C::O_DMA)) : "memory");
-      } else if (eq >= 0) {
-        if (wave < 3)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA + 1) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA) : "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      __syncthreads();
-      slot = slot + 2 >= C::RING ? slot + 2 - C::RING : slot + 2;
-      sq[0] = sq[2];
-      sh[0] = sh[2];
-      sq[1] = sq[3];
-      sh[1] = sh[3];
-      sq[2] = eq;
-      sh[2] = eh;
-      sq[3] = fq;
-      sh[3] = fh;
-    }
-  } else {
   int qb = prev_visible(e.nqb - 1), h = 0;
   int qb1 = qb, h1 = h;
   advance(qb1, h1);
@@ -874,12 +771,12 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
     // index in every stage: hoisted out of the loop they would hold ~40 registers and push the
     // kernel past the 256 that two waves per SIMD allow)
     f32x16 sacc, dacc;
-    dkdv_scores<DQK, DV, true>(qt, kf, vf, sacc, dacc);
+    dkdv_scores<DQK, DV>(qt, kf, vf, sacc, dacc);
     // mask where a row does not see the key (or the key is past the tile's valid keys)
     const bool need_mask = load_uniform_i32(blkmin + qb) < kpos0 + C::BKV - 1 || nvalid < C::BKV || (qb + 1) * kBQ > p.Sq;
     bf16x8 pb[2], dsb[2];
     dkdv_probs<DQK, DV>(qt, need_mask, kk, kpos, nvalid, sacc, dacc, pb, dsb);
-    dkdv_grads<DQK, DV, true>(qt, pb, dsb, dkacc, dvacc);
+    dkdv_grads<DQK, DV>(qt, pb, dsb, dkacc, dvacc);
 
     // the next stage's copies must have landed; the one after may stay in flight
     if (qb2 >= 0)
@@ -892,7 +789,6 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
     h = h1;
     qb1 = qb2;
     h1 = h2;
-  }
   }
 
   // dK = scale dK^T, dV; lane holds key kk, dims 32 m + 8 a4 + 4 hl + t
@@ -919,6 +815,280 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
         *reinterpret_cast<f32x4*>(dvr + 32 * m + 8 * a4 + 4 * hl) = ov;
       }
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dkdv kernel at Dqk = 192: 16 keys per wave on 16x16x32 MFMAs
+// ------------------------------------------------------------------------------------------
+// At 32 keys per wave a Dqk = 192 wave holds 336 registers and runs alone on its SIMD, waiting on
+// its own LDS reads and MFMA results. With 16 keys per wave its K and V fragments (40 registers)
+// and dK, dV accumulators (80) leave room for two waves per SIMD (two 4-wave workgroups of 64
+// keys per CU) at the price of twice the LDS bytes per flop. The stage machinery (ring of 3,
+// copies issued two stages ahead, last row block first) is the 32-key kernel's. Per stage, with
+// lane (key col, group gq) of a wave:
+//  * S = Q K'^T - LSE and dP - D = dO V^T - D per 16-row block mb: the A operands are 16-byte
+//    reads of the Q and dO tiles (row 16 mb + col, dims 32 ks + 8 gq ..), the B operands the
+//    lane's K' and V fragments; lane holds key col, rows 16 mb + 4 gq + r.
+//  * P and dS (bf16) in that order are the B operands of dV^T += dO^T P and dK^T += Q^T dS:
+//    k-slots 8 gq .. 8 gq + 7 are rows 4 gq + 0..3 and 16 + 4 gq + 0..3, and the A operands are
+//    two transposing reads (ds_read_b64_tr_b16) of those rows of the dO and Q tiles per MFMA.
+template <int DQK, int DV>
+struct Dkv16Cfg {
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int KPW = 16;  // keys per wave
+  static constexpr int BKV = WAVES * KPW;
+  static constexpr int QCH = DQK / 8;
+  static constexpr int OCH = DV / 8;
+  static constexpr int Q_BYTES = kBQ * QCH * 16;
+  static constexpr int O_BYTES = kBQ * OCH * 16;
+  static constexpr int STAT_BYTES = 3 * kBQ * 4;  // log2-LSE, D, positions
+  static constexpr int STAGE = Q_BYTES + O_BYTES + STAT_BYTES;
+  static constexpr int Q_DMA = Q_BYTES / (WAVES * 1024);
+  static constexpr int O_DMA = O_BYTES / (WAVES * 1024);
+  static_assert(Q_BYTES % (WAVES * 1024) == 0 && O_BYTES % (WAVES * 1024) == 0, "stage/wave mismatch");
+  static constexpr int KS = DQK / 32;  // k-steps of S
+  static constexpr int VK = DV / 32;   // k-steps of dP
+  static constexpr int MK = DQK / 16;  // 16-dim blocks of dK
+  static constexpr int MV = DV / 16;   // 16-dim blocks of dV
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv16_kernel(DkvParams p, BwdExtra e) {
+  using C = Dkv16Cfg<DQK, DV>;
+  static_assert(C::THREADS == 256, "launch bounds");
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  __shared__ __attribute__((aligned(16))) char lds[kKvStages * C::STAGE];
+
+  // work item (b, g, chunk i, tile t), placed as in the 32-key kernel
+  const int bid = blockIdx.x;
+  const int W = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
+  if (W >= p.n_items) return;
+  int t = W;
+  const int tile = t % p.ntc;
+  t /= p.ntc;
+  const int chunk = t % (2 * p.cp);
+  t /= 2 * p.cp;
+  const int g = t % p.Hkv;
+  const int b = t / p.Hkv;
+  const int t0 = tile * C::BKV;
+  const int kpos0 = chunk * p.c + t0;
+  const int nvalid = min(C::BKV, p.c - t0);
+  const int64_t prow0 = lb_chunk_offset(chunk, p.c, p.cp) + t0;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int col = lane & 15, gq = lane >> 4;
+  const int kk = wave * C::KPW + col;  // this lane's key within the tile
+  const int krow = min(kk, nvalid - 1);
+
+  // K' (scaled) and V fragments, B operands: key kk, dims 32 ks + 8 gq .. + 7
+  bf16x8 kf[C::KS], vf[C::VK];
+  {
+    const bf16x8* kr = reinterpret_cast<const bf16x8*>(p.k + (((int64_t)b * p.S + prow0 + krow) * p.Hkv + g) * DQK);
+    const bf16x8* vr = reinterpret_cast<const bf16x8*>(p.v + (((int64_t)b * p.S + prow0 + krow) * p.Hkv + g) * DV);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 raw = kr[4 * ks + gq];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kf[ks][u] = (__bf16)((float)raw[u] * p.scale_log2);
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::VK; ++ks) vf[ks] = vr[4 * ks + gq];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) asm volatile("" ::"v"(kf[ks]));
+#pragma unroll
+    for (int ks = 0; ks < C::VK; ++ks) asm volatile("" ::"v"(vf[ks]));
+  }
+
+  f32x4 dkacc[C::MK], dvacc[C::MV];
+#pragma unroll
+  for (int m = 0; m < C::MK; ++m) dkacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < C::MV; ++m) dvacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int* blkmin = e.blk;
+  const int* blkmax = e.blk + e.nqb;
+  auto prev_visible = [&](int qb) {
+    while (qb >= 0 && load_uniform_i32(blkmax + qb) < kpos0) --qb;
+    return qb;
+  };
+  const int64_t q_row_bytes = (int64_t)p.Hq * DQK * 2;
+  const int64_t o_row_bytes = (int64_t)p.Hq * DV * 2;
+  const char* qbase = reinterpret_cast<const char*>(p.q) + (int64_t)b * p.Sq * q_row_bytes;
+  const char* obase = reinterpret_cast<const char*>(e.dout) + (int64_t)b * p.Sq * o_row_bytes;
+  const unsigned lds0 = (unsigned)(uintptr_t)lds;
+  // copies of a stage: wave-instruction u fills LDS bytes [1024 (u WAVES + wave), + 1024) of the
+  // Q (or dO) tile, lane l at + 16 l; waves 0, 1, 2 copy the log2-LSE, D and positions
+  auto dma_stage = [&](int qb, int h, int bufi) {
+    const unsigned ql = lds0 + bufi * C::STAGE;
+    const unsigned ol = ql + C::Q_BYTES;
+    const unsigned sl = ol + C::O_BYTES;
+    const int last = p.Sq - 1 - qb * kBQ;  // rows past the shard re-read its last row
+    const char* qt = qbase + (int64_t)qb * kBQ * q_row_bytes + (int64_t)h * DQK * 2;
+    const char* ot = obase + (int64_t)qb * kBQ * o_row_bytes + (int64_t)h * DV * 2;
+#pragma unroll
+    for (int u = 0; u < C::Q_DMA; ++u) {
+      const int pos = (u * C::WAVES + wave) * 1024 + lane * 16;
+      const int row = pos / (C::QCH * 16), phys = (pos % (C::QCH * 16)) / 16;
+      const unsigned off = (unsigned)(min(row, last) * q_row_bytes) + (unsigned)((phys ^ swz<C::QCH>(row)) * 16);
+      dma16_sv(qt, off, ql + (u * C::WAVES + wave) * 1024);
+    }
+#pragma unroll
+    for (int u = 0; u < C::O_DMA; ++u) {
+      const int pos = (u * C::WAVES + wave) * 1024 + lane * 16;
+      const int row = pos / (C::OCH * 16), phys = (pos % (C::OCH * 16)) / 16;
+      const unsigned off = (unsigned)(min(row, last) * o_row_bytes) + (unsigned)((phys ^ swz<C::OCH>(row)) * 16);
+      dma16_sv(ot, off, ol + (u * C::WAVES + wave) * 1024);
+    }
+    if (wave < 3) {
+      const int64_t sidx = ((int64_t)b * p.Hq + h) * e.Sqp + qb * kBQ;
+      const char* src = wave == 0 ? reinterpret_cast<const char*>(e.lse2 + sidx)
+                                  : (wave == 1 ? reinterpret_cast<const char*>(e.delta + sidx)
+                                               : reinterpret_cast<const char*>(e.pos + qb * kBQ));
+      if (lane < 8)
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src + lane * 16),
+                     "s"(sl + wave * 128) : "memory", "m0");
+    }
+  };
+  auto wait_all_but_one_stage = [&]() {
+    if (wave < 3)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA + 1) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::Q_DMA + C::O_DMA) : "memory");
+  };
+  auto advance = [&](int& sqb, int& sh) {
+    if (sqb < 0) return;
+    if (++sh == p.G) {
+      sh = 0;
+      sqb = prev_visible(sqb - 1);
+    }
+  };
+  const int kpos = kpos0 + kk;
+
+  int qb = prev_visible(e.nqb - 1), h = 0;
+  int qb1 = qb, h1 = h;
+  advance(qb1, h1);
+  if (qb >= 0) dma_stage(qb, g * p.G + h, 0);
+  if (qb1 >= 0) {
+    dma_stage(qb1, g * p.G + h1, 1);
+    wait_all_but_one_stage();
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  int buf = 0;
+  while (qb >= 0) {
+    int qb2 = qb1, h2 = h1;
+    advance(qb2, h2);
+    const int buf2 = buf >= kKvStages - 2 ? buf + 2 - kKvStages : buf + 2;
+    if (qb2 >= 0) dma_stage(qb2, g * p.G + h2, buf2);  // that slot was last read two stages ago
+
+    const char* qt = lds + buf * C::STAGE;
+    const char* ot = qt + C::Q_BYTES;
+    const float* st_lse = reinterpret_cast<const float*>(ot + C::O_BYTES);
+    const float* st_dlt = st_lse + kBQ;
+    const int* st_pos = reinterpret_cast<const int*>(st_dlt + kBQ);
+    const bool need_mask = load_uniform_i32(blkmin + qb) < kpos0 + C::BKV - 1 || nvalid < C::BKV || (qb + 1) * kBQ > p.Sq;
+
+    // ---- S - LSE and dP - D, then P and dS (bf16) in the B-operand order of the gradients
+    bf16x8 pb, dsb;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int row = 16 * mb + col;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(st_lse + 16 * mb + 4 * gq);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st_dlt + 16 * mb + 4 * gq);
+      f32x4 sacc = -l4, dacc = -d4;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qt + row * (C::QCH * 16) + (((4 * ks + gq) ^ swz<C::QCH>(row)) << 4));
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[ks], sacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::VK; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ot + row * (C::OCH * 16) + (((4 * ks + gq) ^ swz<C::OCH>(row)) << 4));
+        dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vf[ks], dacc, 0, 0, 0);
+      }
+      if (need_mask) {
+        const int4 q4 = *reinterpret_cast<const int4*>(st_pos + 16 * mb + 4 * gq);
+        const int qp[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[r] = (kk < nvalid && kpos <= qp[r]) ? sacc[r] : -INFINITY;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(sacc[r]);
+        pb[4 * mb + r] = (__bf16)pr;
+        dsb[4 * mb + r] = (__bf16)(pr * dacc[r]);
+      }
+    }
+
+    // ---- dV^T += dO^T P and dK^T += Q^T dS: lane 4 e + q of group gq reads rows 4 gq + e and
+    // 16 + 4 gq + e, dims 16 m + 4 q .. + 3 of the tile
+    {
+      const int e4 = (lane & 15) >> 2, q4 = lane & 3;
+      const int rlo = 4 * gq + e4, rhi = rlo + 16;
+      const int within = 8 * (q4 & 1);
+#pragma unroll
+      for (int m = 0; m < C::MV; ++m) {
+        const int c = 2 * m + (q4 >> 1);
+        const char* alo = ot + rlo * (C::OCH * 16) + ((c ^ swz<C::OCH>(rlo)) << 4) + within;
+        const char* ahi = ot + rhi * (C::OCH * 16) + ((c ^ swz<C::OCH>(rhi)) << 4) + within;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(alo));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(ahi));
+        const i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dvacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cat), pb, dvacc[m], 0, 0, 0);
+      }
+#pragma unroll
+      for (int m = 0; m < C::MK; ++m) {
+        const int c = 2 * m + (q4 >> 1);
+        const char* alo = qt + rlo * (C::QCH * 16) + ((c ^ swz<C::QCH>(rlo)) << 4) + within;
+        const char* ahi = qt + rhi * (C::QCH * 16) + ((c ^ swz<C::QCH>(rhi)) << 4) + within;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(alo));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(ahi));
+        const i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dkacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cat), dsb, dkacc[m], 0, 0, 0);
+      }
+    }
+
+    // the next stage's copies must have landed; the one after may stay in flight
+    if (qb2 >= 0)
+      wait_all_but_one_stage();
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    buf = buf + 1 == kKvStages ? 0 : buf + 1;
+    qb = qb1;
+    h = h1;
+    qb1 = qb2;
+    h1 = h2;
+  }
+
+  // dK = scale dK^T, dV; lane holds key kk, dims 16 m + 4 gq + r
+  if (kk < nvalid) {
+    float* dkr = e.dk + (((int64_t)b * p.S + prow0 + kk) * p.Hkv + g) * DQK;
+    float* dvr = e.dv + (((int64_t)b * p.S + prow0 + kk) * p.Hkv + g) * DV;
+#pragma unroll
+    for (int m = 0; m < C::MK; ++m) {
+      f32x4 ov;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ov[u] = dkacc[m][u] * e.scale;
+      *reinterpret_cast<f32x4*>(dkr + 16 * m + 4 * gq) = ov;
+    }
+#pragma unroll
+    for (int m = 0; m < C::MV; ++m) *reinterpret_cast<f32x4*>(dvr + 16 * m + 4 * gq) = dvacc[m];
+  }
+}
+
+// Keys per dkdv workgroup: the 16-keys-per-wave kernel at Dqk > 128, else the 32-key one.
+template <int DQK, int DV>
+constexpr int dkdv_keys_per_wg() {
+  if constexpr (DQK > 128) {
+    return Dkv16Cfg<DQK, DV>::BKV;
+  } else {
+    return KvShape<DQK>::BKV;
   }
 }
 
@@ -992,15 +1162,23 @@ hipError_t launch_bwd_typed(const AttnBwdArgs& a, hipStream_t stream) {
   d.G = a.hq / a.hkv;
   d.cp = a.cp;
   d.c = a.seq / (2 * a.cp);
-  d.ntc = (d.c + KvShape<DQK>::BKV - 1) / KvShape<DQK>::BKV;
+  // Dqk = 192: the 16-keys-per-wave kernel (two waves per SIMD)
+  constexpr bool kKeys16 = DQK > 128;
+  constexpr int kBkv = dkdv_keys_per_wg<DQK, DV>();
+  d.ntc = (d.c + kBkv - 1) / kBkv;
   d.n_items = 2 * a.cp * d.B * d.Hkv * d.ntc;
   d.per_xcd = (d.n_items + kNumXcd - 1) / kNumXcd;
   d.scale_log2 = a.scale * kLog2e;
   d.q = static_cast<const __bf16*>(a.q);
   d.k = static_cast<const __bf16*>(a.k);
   d.v = static_cast<const __bf16*>(a.v);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV>), dim3(d.per_xcd * kNumXcd), dim3(KvShape<DQK>::THREADS), 0,
-                     stream, d, e);
+  if constexpr (kKeys16) {
+    hipLaunchKernelGGL((attn_bwd_dkdv16_kernel<DQK, DV>), dim3(d.per_xcd * kNumXcd), dim3(Dkv16Cfg<DQK, DV>::THREADS),
+                       0, stream, d, e);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV>), dim3(d.per_xcd * kNumXcd), dim3(KvShape<DQK>::THREADS), 0,
+                       stream, d, e);
+  }
   return hipGetLastError();
 }
 

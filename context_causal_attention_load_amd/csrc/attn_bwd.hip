@@ -854,6 +854,23 @@ struct Dkv16Cfg {
   static constexpr int MV = DV / 16;   // 16-dim blocks of dV
 };
 
+// Chunk swizzle of the 16-key kernel's tiles (a 16-byte chunk c of row r sits at c ^ swz16(r)).
+// LDS serves 256 bytes a cycle: a 16-byte read is served 16 lanes at a time, an 8-byte read 32.
+// The S reads take one chunk of 16 consecutive rows, so swz16 is one-to-one on those (with a
+// 384-byte row at Dqk 192, separately on even and odd rows, which sit 128 bytes apart). A
+// transposing read takes a chunk pair {2 m, 2 m + 1} of rows 8 k .. 8 k + 7, so swz16 / 2 is
+// one-to-one on those rows (at Dqk 192 again separately on even and odd rows). The 32-key
+// kernel's swizzle spreads only rows 0..3 apart, which its transposing reads need.
+template <int CH>
+__device__ __forceinline__ int swz16(int row) {
+  static_assert(CH % 16 == 0 || CH % 16 == 8, "tiles of 16 or 24 chunks per row");
+  if constexpr (CH % 16 == 0) {
+    return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
+  } else {
+    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+  }
+}
+
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv16_kernel(DkvParams p, BwdExtra e) {
   using C = Dkv16Cfg<DQK, DV>;
@@ -933,14 +950,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv16_kernel(DkvParams p, Bw
     for (int u = 0; u < C::Q_DMA; ++u) {
       const int pos = (u * C::WAVES + wave) * 1024 + lane * 16;
       const int row = pos / (C::QCH * 16), phys = (pos % (C::QCH * 16)) / 16;
-      const unsigned off = (unsigned)(min(row, last) * q_row_bytes) + (unsigned)((phys ^ swz<C::QCH>(row)) * 16);
+      const unsigned off = (unsigned)(min(row, last) * q_row_bytes) + (unsigned)((phys ^ swz16<C::QCH>(row)) * 16);
       dma16_sv(qt, off, ql + (u * C::WAVES + wave) * 1024);
     }
 #pragma unroll
     for (int u = 0; u < C::O_DMA; ++u) {
       const int pos = (u * C::WAVES + wave) * 1024 + lane * 16;
       const int row = pos / (C::OCH * 16), phys = (pos % (C::OCH * 16)) / 16;
-      const unsigned off = (unsigned)(min(row, last) * o_row_bytes) + (unsigned)((phys ^ swz<C::OCH>(row)) * 16);
+      const unsigned off = (unsigned)(min(row, last) * o_row_bytes) + (unsigned)((phys ^ swz16<C::OCH>(row)) * 16);
       dma16_sv(ot, off, ol + (u * C::WAVES + wave) * 1024);
     }
     if (wave < 3) {
@@ -1003,12 +1020,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv16_kernel(DkvParams p, Bw
       f32x4 sacc = -l4, dacc = -d4;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qt + row * (C::QCH * 16) + (((4 * ks + gq) ^ swz<C::QCH>(row)) << 4));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qt + row * (C::QCH * 16) + (((4 * ks + gq) ^ swz16<C::QCH>(row)) << 4));
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[ks], sacc, 0, 0, 0);
       }
 #pragma unroll
       for (int ks = 0; ks < C::VK; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ot + row * (C::OCH * 16) + (((4 * ks + gq) ^ swz<C::OCH>(row)) << 4));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ot + row * (C::OCH * 16) + (((4 * ks + gq) ^ swz16<C::OCH>(row)) << 4));
         dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vf[ks], dacc, 0, 0, 0);
       }
       if (need_mask) {
@@ -1034,8 +1051,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv16_kernel(DkvParams p, Bw
 #pragma unroll
       for (int m = 0; m < C::MV; ++m) {
         const int c = 2 * m + (q4 >> 1);
-        const char* alo = ot + rlo * (C::OCH * 16) + ((c ^ swz<C::OCH>(rlo)) << 4) + within;
-        const char* ahi = ot + rhi * (C::OCH * 16) + ((c ^ swz<C::OCH>(rhi)) << 4) + within;
+        const char* alo = ot + rlo * (C::OCH * 16) + ((c ^ swz16<C::OCH>(rlo)) << 4) + within;
+        const char* ahi = ot + rhi * (C::OCH * 16) + ((c ^ swz16<C::OCH>(rhi)) << 4) + within;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(alo));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(ahi));
         const i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -1044,8 +1061,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv16_kernel(DkvParams p, Bw
 #pragma unroll
       for (int m = 0; m < C::MK; ++m) {
         const int c = 2 * m + (q4 >> 1);
-        const char* alo = qt + rlo * (C::QCH * 16) + ((c ^ swz<C::QCH>(rlo)) << 4) + within;
-        const char* ahi = qt + rhi * (C::QCH * 16) + ((c ^ swz<C::QCH>(rhi)) << 4) + within;
+        const char* alo = qt + rlo * (C::QCH * 16) + ((c ^ swz16<C::QCH>(rlo)) << 4) + within;
+        const char* ahi = qt + rhi * (C::QCH * 16) + ((c ^ swz16<C::QCH>(rhi)) << 4) + within;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(alo));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(ahi));
         const i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};

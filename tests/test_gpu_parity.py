@@ -640,6 +640,17 @@ def test_backward_mla_shape_small():
     check_bwd_full(1, 768, 2, 4, 4, 192, (0, 1), seed=23, tag="MLA Dqk192 Dv128", d_v=128)
 
 
+@pytest.mark.parametrize("batch,seq,hq,hkv,ranks", [
+    (1, 640, 8, 2, (0, 1)),  # G = 4, c = 160: two 64-key tiles and a 32-key tail per chunk
+    (2, 312, 6, 3, (1,)),    # G = 2, batch 2, c = 78
+])
+def test_backward_mla_dims_grouped_heads(batch, seq, hq, hkv, ranks):
+    """Dqk 192, Dv 128 with several query heads per kv head: the dkdv kernel at these head dims
+    walks the query heads of its kv head inside its stage loop, and dq reads the shared K/V."""
+    check_bwd_full(batch, seq, 2, hq, hkv, 192, ranks, seed=seq + 7 * hq, d_v=128,
+                   tag=f"B{batch} S{seq} Hq{hq}/{hkv} Dqk192 Dv128")
+
+
 def test_backward_contiguous_shard_positions():
     """Explicit q_positions: a contiguous (unbalanced) shard of the natural order, K/V natural."""
     seq, hq, hkv, d = 512, 4, 2, 64

@@ -104,6 +104,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(FwdParams p, BwdExtra e)
 // ------------------------------------------------------------------------------------------
 constexpr int kDqTileKeys = 64;  // keys per K/V tile of the dq kernel
 
+// A compile-time buffer index for loops unrolled over a double buffer.
+template <int V>
+struct BufTag {
+  static constexpr int value = V;
+};
+
 template <int DQK, int DV>
 struct DqCfg {
   static constexpr int BK = kDqTileKeys;
@@ -254,6 +260,110 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
   if (t_beg < t_end) dma_tile(tc, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+
+  if constexpr (DQK > 128) {
+    // Dqk = 192, Dv = 128: every LDS read is a lane-constant register plus an immediate. Rows of
+    // the K tile hold 24 chunks, whose swizzle (< 8) only permutes the low three bits of a chunk
+    // index; rows of the V tile are 256 bytes, so a row start has eight zero low bits and its
+    // chunk offset can be flipped with one xor. With the tile loop unrolled by two, the double
+    // buffer's offset is an immediate as well. (Recomputing these offsets for every read, as the
+    // loop for the smaller head dims may, costs more vector instructions than the matrix
+    // products take.)
+    static_assert(C::KCH % 16 == 8 && C::VCH == 16, "layout of this loop");
+    const int r31 = lane & 31, lgrp = lane >> 4, ltr_e = (lane & 15) >> 2, ltr_q = lane & 3;
+    // S^T = K Q'^T: block mb, k-step ks reads kb + mb 32 rows + 128 (ks / 4) + kso[ks % 4]
+    const int swk = swz<C::KCH>(r31);
+    int kso[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kso[j] = r31 * (C::KCH * 16) + (((2 * j + hl) ^ swk) << 4);
+    // dP^T = V dO^T: k-step ks reads vb + mb 32 rows + (vso ^ 32 ks)
+    const int vso = r31 * (C::VCH * 16) + (((hl ^ swz<C::VCH>(r31)) & 15) << 4);
+    // dQ^T += K^T dS^T: k-step ks, dims block m read rows 16 ks + ra0 (+ 8) at
+    // kb + 16 ks rows + 128 (m / 2) + tra[m % 2] (trb[m % 2])
+    const int ra0 = 4 * (lgrp >> 1) + ltr_e;
+    const int c0 = 2 * (lgrp & 1) + (ltr_q >> 1), within = 8 * (ltr_q & 1);
+    int tra[2], trb[2];
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      tra[mm] = ra0 * (C::KCH * 16) + (((4 * mm + c0) ^ swz<C::KCH>(ra0)) << 4) + within;
+      trb[mm] = (ra0 + 8) * (C::KCH * 16) + (((4 * mm + c0) ^ swz<C::KCH>(ra0 + 8)) << 4) + within;
+    }
+
+    auto tile = [&](auto tag, const TileCursor& cur, const TileCursor& nxt, bool has_next) {
+      constexpr int B = decltype(tag)::value;
+      if (has_next) dma_tile(nxt, B ^ 1);
+      const char* kb = lds + B * C::STAGE;
+      const char* vb = kb + C::K_BYTES;
+      const int kpos0 = cur.chunk * c + cur.t0;
+      const int nvalid = min(C::BK, c - cur.t0);
+      const bool need_mask = (kpos0 + C::BK - 1 > qmin) || (nvalid < C::BK);
+      // key kk of the tile is visible iff kk <= lim (kk < nvalid and kpos0 + kk <= my_pos)
+      const int lim = min(nvalid - 1, my_pos - kpos0) - 4 * hl;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        f32x16 sacc, dacc;
+        // opaque copies, so the fills are not hoisted out of the loop as full vectors
+        float nl = neg_l2, nd = neg_d;
+        asm volatile("" : "+v"(nl), "+v"(nd));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[r] = nl;
+          dacc[r] = nd;
+        }
+        const char* kr = kb + mb * 32 * (C::KCH * 16);
+#pragma unroll
+        for (int ks = 0; ks < C::QK_STEPS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 128 * (ks / 4) + kso[ks % 4]);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc, 0, 0, 0);
+        }
+        const char* vr = vb + mb * 32 * (C::VCH * 16);
+#pragma unroll
+        for (int ks = 0; ks < C::DV_STEPS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vr + (vso ^ (32 * ks)));
+          dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[ks], dacc, 0, 0, 0);
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = mb * 32 + 8 * (r / 4) + (r % 4);
+            sacc[r] = kk <= lim ? sacc[r] : -INFINITY;
+          }
+        }
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dsb[r / 8][r % 8] = (__bf16)(__builtin_amdgcn_exp2f(sacc[r]) * dacc[r]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const char* kt = kb + 16 * (2 * mb + j) * (C::KCH * 16);
+#pragma unroll
+          for (int m = 0; m < C::MQ; ++m) {
+            const char* pa = kt + 128 * (m / 2) + tra[m % 2];
+            const char* pb2 = kt + 128 * (m / 2) + trb[m % 2];
+            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pa));
+            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(pb2));
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            dqacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), dsb[j], dqacc[m], 0,
+                                                               0, 0);
+          }
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    };
+    for (int t = t_beg; t < t_end;) {
+      TileCursor nx = tc;
+      next_tile<C::BK>(nx, c, qmax);
+      tile(BufTag<0>{}, tc, nx, t + 1 < t_end);
+      tc = nx;
+      if (++t == t_end) break;
+      nx = tc;
+      next_tile<C::BK>(nx, c, qmax);
+      tile(BufTag<1>{}, tc, nx, t + 1 < t_end);
+      tc = nx;
+      ++t;
+    }
+  } else {
   int buf = 0;
 
   for (int t = t_beg; t < t_end; ++t) {
@@ -346,6 +456,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
     __syncthreads();
     buf ^= 1;
     tc = nx;
+  }
   }
 
   if (my_row < p.Sq) {

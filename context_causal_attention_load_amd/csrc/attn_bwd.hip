@@ -1096,6 +1096,25 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv16_kernel(DkvParams p, Bw
   };
   const int kpos = kpos0 + kk;
 
+  // Lane-constant LDS offsets of the reads within a slot, so that each read is one register
+  // plus an immediate. swz16 of a row depends on its bits 0..3 only, so rows 16 mb + col, and
+  // rows rlo and rlo + 16, share it; with 24 chunks per Q row the swizzle (< 8) only permutes the
+  // low three bits of a chunk index.
+  static_assert(C::QCH % 16 == 8 && C::OCH == 16, "layout of the offsets below");
+  const int e4 = (lane & 15) >> 2, q4 = lane & 3;
+  const int rlo = 4 * gq + e4;
+  const int within = 8 * (q4 & 1), cx = q4 >> 1;
+  int qso[2], oso[C::VK], tqo[4], too[C::MV];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) qso[j] = col * (C::QCH * 16) + (((4 * j + gq) ^ swz16<C::QCH>(col)) << 4);
+#pragma unroll
+  for (int ks = 0; ks < C::VK; ++ks) oso[ks] = col * (C::OCH * 16) + (((4 * ks + gq) ^ swz16<C::OCH>(col)) << 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) tqo[j] = rlo * (C::QCH * 16) + (((2 * j + cx) ^ swz16<C::QCH>(rlo)) << 4) + within;
+#pragma unroll
+  for (int m = 0; m < C::MV; ++m)
+    too[m] = C::Q_BYTES + rlo * (C::OCH * 16) + (((2 * m + cx) ^ swz16<C::OCH>(rlo)) << 4) + within;
+
   int qb = prev_visible(e.nqb - 1), h = 0;
   int qb1 = qb, h1 = h;
   advance(qb1, h1);
@@ -1125,18 +1144,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv16_kernel(DkvParams p, Bw
     bf16x8 pb, dsb;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const int row = 16 * mb + col;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(st_lse + 16 * mb + 4 * gq);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(st_dlt + 16 * mb + 4 * gq);
       f32x4 sacc = -l4, dacc = -d4;
+      // Q: chunk 4 ks + gq of row 16 mb + col is at 8 (ks / 2) + ((4 (ks % 2) + gq) ^ swz16)
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qt + row * (C::QCH * 16) + (((4 * ks + gq) ^ swz16<C::QCH>(row)) << 4));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qt + 16 * mb * (C::QCH * 16) + 128 * (ks / 2) + qso[ks % 2]);
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[ks], sacc, 0, 0, 0);
       }
 #pragma unroll
       for (int ks = 0; ks < C::VK; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ot + row * (C::OCH * 16) + (((4 * ks + gq) ^ swz16<C::OCH>(row)) << 4));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ot + 16 * mb * (C::OCH * 16) + oso[ks]);
         dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vf[ks], dacc, 0, 0, 0);
       }
       if (need_mask) {
@@ -1156,26 +1175,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv16_kernel(DkvParams p, Bw
     // ---- dV^T += dO^T P and dK^T += Q^T dS: lane 4 e + q of group gq reads rows 4 gq + e and
     // 16 + 4 gq + e, dims 16 m + 4 q .. + 3 of the tile
     {
-      const int e4 = (lane & 15) >> 2, q4 = lane & 3;
-      const int rlo = 4 * gq + e4, rhi = rlo + 16;
-      const int within = 8 * (q4 & 1);
+      // row rlo + 16 sits 16 rows after row rlo, at the same chunk
 #pragma unroll
       for (int m = 0; m < C::MV; ++m) {
-        const int c = 2 * m + (q4 >> 1);
-        const char* alo = ot + rlo * (C::OCH * 16) + ((c ^ swz16<C::OCH>(rlo)) << 4) + within;
-        const char* ahi = ot + rhi * (C::OCH * 16) + ((c ^ swz16<C::OCH>(rhi)) << 4) + within;
+        const char* alo = qt + too[m];
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(alo));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(ahi));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(alo + 16 * (C::OCH * 16)));
         const i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         dvacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cat), pb, dvacc[m], 0, 0, 0);
       }
+      // Q: chunk 2 m + cx of row rlo is at 8 (m / 4) + ((2 (m % 4) + cx) ^ swz16)
 #pragma unroll
       for (int m = 0; m < C::MK; ++m) {
-        const int c = 2 * m + (q4 >> 1);
-        const char* alo = qt + rlo * (C::QCH * 16) + ((c ^ swz16<C::QCH>(rlo)) << 4) + within;
-        const char* ahi = qt + rhi * (C::QCH * 16) + ((c ^ swz16<C::QCH>(rhi)) << 4) + within;
+        const char* alo = qt + 128 * (m / 4) + tqo[m % 4];
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(alo));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(ahi));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(alo + 16 * (C::QCH * 16)));
         const i16x8 cat = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         dkacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cat), dsb, dkacc[m], 0, 0, 0);
       }

@@ -41,8 +41,8 @@ struct BwdExtra {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;   // [B, Hq, Sqp]
-  float* lse2;    // [B, Hq, Sqp]
+  float* neg_delta;  // [B, Hq, Sqp]: -D, the seed of dP - D
+  float* neg_lse2;   // [B, Hq, Sqp]: -log2(e) LSE, the seed of the exponents of P
   int32_t* pos;   // [Sqp]
   int32_t* blk;   // [2 * nqb]: min positions, then max positions
   int Sqp, nqb;
@@ -71,7 +71,8 @@ __global__ __launch_bounds__(256) void bwd_positions_kernel(FwdParams p, BwdExtr
   }
 }
 
-// ---- prep: D = dO . O and LSE * log2 e per (b, h, row); 16 lanes per row
+// ---- prep: -D = -dO . O and -LSE * log2 e per (b, h, row), stored negated so that they seed the
+// matrix products as they are; 16 lanes per row
 template <int DV>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(FwdParams p, BwdExtra e) {
   const int64_t r = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;  // (b, h, row) over padded rows
@@ -94,8 +95,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(FwdParams p, BwdExtra e)
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
   if (l16 == 0) {
-    e.delta[r] = acc;
-    e.lse2[r] = row < p.Sq ? e.lse[bh * p.Sq + row] * kLog2e : 0.f;
+    e.neg_delta[r] = -acc;
+    e.neg_lse2[r] = row < p.Sq ? -e.lse[bh * p.Sq + row] * kLog2e : 0.f;
   }
 }
 
@@ -165,8 +166,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(FwdParams p, B
 #pragma unroll
     for (int ks = 0; ks < C::DV_STEPS; ++ks) df[ks] = drow[2 * ks + hl];
     const int64_t sidx = ((int64_t)w.b * p.Hq + head) * e.Sqp + row;
-    neg_l2 = -e.lse2[sidx];
-    neg_d = -e.delta[sidx];
+    neg_l2 = e.neg_lse2[sidx];
+    neg_d = e.neg_delta[sidx];
 #pragma unroll
     for (int ks = 0; ks < C::QK_STEPS; ++ks) asm volatile("" ::"v"(qf[ks]));
 #pragma unroll
@@ -625,8 +626,8 @@ __device__ __forceinline__ void dkdv_scores(const char* qt, const bf16x8 (&kf)[D
     const f32x4 d4 = *reinterpret_cast<const f32x4*>(st_dlt + 8 * i + 4 * lhl);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sacc[4 * i + j] = -l4[j];
-      dacc[4 * i + j] = -d4[j];
+      sacc[4 * i + j] = l4[j];
+      dacc[4 * i + j] = d4[j];
     }
   }
   const char* qr = qt + row * (C::QCH * 16);
@@ -832,8 +833,8 @@ __global__ __launch_bounds__(KvShape<DQK>::THREADS, KvShape<DQK>::MIN_WG_PER_CU)
     // array each with 8 lanes
     if (wave < 3) {
       const int64_t sidx = ((int64_t)b * p.Hq + h) * e.Sqp + qb * kBQ;
-      const char* src = wave == 0 ? reinterpret_cast<const char*>(e.lse2 + sidx)
-                                  : (wave == 1 ? reinterpret_cast<const char*>(e.delta + sidx)
+      const char* src = wave == 0 ? reinterpret_cast<const char*>(e.neg_lse2 + sidx)
+                                  : (wave == 1 ? reinterpret_cast<const char*>(e.neg_delta + sidx)
                                                : reinterpret_cast<const char*>(e.pos + qb * kBQ));
       if (lane < 8)
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src + lane * 16),
@@ -1073,8 +1074,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv16_kernel(DkvParams p, Bw
     }
     if (wave < 3) {
       const int64_t sidx = ((int64_t)b * p.Hq + h) * e.Sqp + qb * kBQ;
-      const char* src = wave == 0 ? reinterpret_cast<const char*>(e.lse2 + sidx)
-                                  : (wave == 1 ? reinterpret_cast<const char*>(e.delta + sidx)
+      const char* src = wave == 0 ? reinterpret_cast<const char*>(e.neg_lse2 + sidx)
+                                  : (wave == 1 ? reinterpret_cast<const char*>(e.neg_delta + sidx)
                                                : reinterpret_cast<const char*>(e.pos + qb * kBQ));
       if (lane < 8)
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src + lane * 16),
@@ -1146,7 +1147,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv16_kernel(DkvParams p, Bw
     for (int mb = 0; mb < 2; ++mb) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(st_lse + 16 * mb + 4 * gq);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(st_dlt + 16 * mb + 4 * gq);
-      f32x4 sacc = -l4, dacc = -d4;
+      f32x4 sacc = l4, dacc = d4;
       // Q: chunk 4 ks + gq of row 16 mb + col is at 8 (ks / 2) + ((4 (ks % 2) + gq) ^ swz16)
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
@@ -1253,8 +1254,8 @@ hipError_t launch_bwd_typed(const AttnBwdArgs& a, hipStream_t stream) {
   e.scale = a.scale;
   char* ws = static_cast<char*>(a.ws);
   const size_t stat_bytes = (size_t)a.batch * a.hq * Sqp * 4;
-  e.delta = reinterpret_cast<float*>(ws);
-  e.lse2 = reinterpret_cast<float*>(ws + stat_bytes);
+  e.neg_delta = reinterpret_cast<float*>(ws);
+  e.neg_lse2 = reinterpret_cast<float*>(ws + stat_bytes);
   e.pos = reinterpret_cast<int32_t*>(ws + 2 * stat_bytes);
   e.blk = reinterpret_cast<int32_t*>(ws + 2 * stat_bytes + (size_t)Sqp * 4);
 

@@ -11,15 +11,17 @@
 // reduce-scatter over ranks would sum).
 //
 // Three launches, bf16 inputs, fp32 accumulation, fp32 gradients:
-//  * prep: D, LSE in log2 units and the rows' positions (padded to 32-row blocks) into the
-//    workspace, plus each 32-row block's smallest and largest position.
+//  * prep: -D and -LSE in log2 units (negated, so that they seed the products as they are) and
+//    the rows' positions (padded to 32-row blocks) into the workspace, plus each 32-row block's
+//    smallest and largest position.
 //  * dq: the forward's decomposition (a wave owns one head and 32 query rows; K/V tiles of 64
 //    keys stream through double-buffered LDS by direct-to-LDS copies, visited chunk by chunk
 //    in original order). Per tile: S^T = K Q'^T seeded with -LSE (so the products are the
 //    exponents of P), dP^T - D = V dO^T seeded with -D, dS^T = P^T (dP^T - D) rounded to bf16,
 //    then dQ^T += K^T dS^T with K^T from the transposing LDS read (ds_read_b64_tr_b16).
 //  * dkdv: key-stationary. A workgroup owns 32 keys per wave of one kv head (256 keys at
-//    Dqk = 128, else 128); the keys' K' (scaled) and V fragments stay in registers as B operands.
+//    Dqk = 128, 128 at Dqk = 64); the keys' K' (scaled) and V fragments stay in registers as B
+//    operands.
 //    It streams (32-row query block, query head) stages of Q, dO, log2-LSE, D and positions
 //    through an LDS ring of 3 slots, skipping blocks whose rows are all before the keys. (At
 //    Dqk = 192 a variant with 16 keys per wave on 16x16x32 MFMAs keeps two waves per SIMD.)

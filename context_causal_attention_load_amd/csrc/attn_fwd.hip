@@ -44,18 +44,23 @@ namespace {
 // ------------------------------------------------------------------------------------------
 // bf16 kernel
 // ------------------------------------------------------------------------------------------
-// Keys per tile: 128 where two stages of K and V fit the 160 KB of LDS, else 64.
+// Keys per tile: 128 where two stages of K and V fit in 128 KB of LDS, else 96 where they fit
+// in 120 KB (Dqk 192, Dv 128).
+constexpr int bf16_bk(int dqk, int dv) { return 2 * 128 * (dqk + dv) * 2 <= 128 * 1024 ? 128 : 96; }
 template <int DQK, int DV>
 struct Bf16Cfg {
-  static constexpr int BK = (2 * 128 * (DQK + DV) * 2 <= 128 * 1024) ? 128 : 64;
+  static constexpr int BK = bf16_bk(DQK, DV);
   static constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
   static constexpr int VCH = DV / 8;
   static constexpr int K_BYTES = BK * KCH * 16;
   static constexpr int V_BYTES = BK * VCH * 16;
   static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int K_LOADS = BK * KCH / kThreads;
+  // 1 KB wave-copies of the K tile per wave; at 96 keys x 24 chunks the last one is taken by
+  // the first half of the waves only
+  static constexpr int K_LOADS = (BK * KCH + kThreads - 1) / kThreads;
+  static constexpr bool K_PART = BK * KCH % kThreads != 0;
   static constexpr int V_LOADS = BK * VCH / kThreads;
-  static_assert(BK * KCH % kThreads == 0 && BK * VCH % kThreads == 0, "tile/thread mismatch");
+  static_assert(BK * KCH % (kThreads / 2) == 0 && BK * VCH % kThreads == 0, "tile/thread mismatch");
   static constexpr int QK_STEPS = DQK / 16;
   static constexpr int MV = DV / 32;
   static constexpr int MB = BK / 32;   // 32-key blocks of S^T
@@ -149,13 +154,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdParams p)
     const unsigned vl = kl + C::K_BYTES;
     if (last == C::BK - 1) {
 #pragma unroll
-      for (int u = 0; u < K_DMA; ++u) dma16_sv(kt, k_off[u], kl + (u * kWaves + wave) * 1024);
+      for (int u = 0; u < K_DMA; ++u)
+        if (!C::K_PART || u + 1 < K_DMA || wave < kWaves / 2) dma16_sv(kt, k_off[u], kl + (u * kWaves + wave) * 1024);
 #pragma unroll
       for (int u = 0; u < V_DMA; ++u) dma16_sv(vt, v_off[u], vl + (u * kWaves + wave) * 1024);
     } else {  // a chunk's partial last tile: rows past it re-read its last row (finite, masked)
 #pragma unroll
       for (int u = 0; u < K_DMA; ++u)
-        dma16_sv(kt, (unsigned)(min(k_row[u], last) * kv_row_bytes_k) + k_col[u], kl + (u * kWaves + wave) * 1024);
+        if (!C::K_PART || u + 1 < K_DMA || wave < kWaves / 2)
+          dma16_sv(kt, (unsigned)(min(k_row[u], last) * kv_row_bytes_k) + k_col[u], kl + (u * kWaves + wave) * 1024);
 #pragma unroll
       for (int u = 0; u < V_DMA; ++u)
         dma16_sv(vt, (unsigned)(min(v_row[u], last) * kv_row_bytes_v) + v_col[u], vl + (u * kWaves + wave) * 1024);
@@ -565,7 +572,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(FwdParams p) 
 // write unnormalised partials and a merge kernel combines them by their running maxima (as the
 // decode does).
 // ------------------------------------------------------------------------------------------
-int bf16_tile_keys(int d_qk, int d_v) { return (2 * 128 * (d_qk + d_v) * 2 <= 128 * 1024) ? 128 : 64; }
+int bf16_tile_keys(int d_qk, int d_v) { return bf16_bk(d_qk, d_v); }
 
 constexpr int kSplitMinTiles = 8;  // no piece below this many key tiles
 

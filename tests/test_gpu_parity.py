@@ -87,6 +87,10 @@ SMALL = [
     ("fp32-d128", 1, 256, (2,), 2, 2, 128, 128, torch.float32, 17),
     ("chunk1-bf16", 1, 4, (2, 1), 1, 1, 64, 64, torch.bfloat16, 18),
     ("chunk1-cp4-fp32", 1, 8, (4,), 2, 1, 64, 64, torch.float32, 19),
+    # Dqk 192 runs 96-key tiles: a chunk of exactly one tile, one key past it, one short of two
+    ("mla-c96-bf16", 1, 384, (2,), 2, 2, 192, 128, torch.bfloat16, 20),
+    ("mla-c97-g2-bf16", 1, 388, (2,), 4, 2, 192, 128, torch.bfloat16, 21),
+    ("mla-c191-cp3-bf16", 1, 1146, (3,), 2, 1, 192, 128, torch.bfloat16, 22),
 ]
 
 
@@ -643,6 +647,7 @@ def test_backward_mla_shape_small():
 @pytest.mark.parametrize("batch,seq,hq,hkv,ranks", [
     (1, 640, 8, 2, (0, 1)),  # G = 4, c = 160: two 64-key tiles and a 32-key tail per chunk
     (2, 312, 6, 3, (1,)),    # G = 2, batch 2, c = 78
+    (1, 388, 4, 2, (0, 1)),  # c = 97: one 64-key tile and a 33-key tail per chunk
 ])
 def test_backward_mla_dims_grouped_heads(batch, seq, hq, hkv, ranks):
     """Dqk 192, Dv 128 with several query heads per kv head: the dkdv kernel at these head dims

@@ -250,6 +250,42 @@ def _time_calls(call, iters):
     return ms, t0.elapsed_time(t1) / iters
 
 
+def _time_graph(call, check, reps=24, replays=10):
+    """GPU time per call of a short call: ``reps`` calls captured in one HIP graph and replayed
+    ``replays`` times between one pair of events, so the host's per-call launch cost does not
+    enter (for calls of a few microseconds it exceeds the kernels). ``check()`` returns the
+    call's outputs; after the replays they must equal those of an eager call bit for bit, else
+    the figure is withheld (None)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            call(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = [x.clone() for x in check()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    call(reps - 1)  # eager again: the last captured call's inputs
+    torch.cuda.synchronize()
+    eager_last = [x.clone() for x in check()]
+    g.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(eager_last, check()))
+    del g, eager
+    return t0.elapsed_time(t1) / (replays * reps) if same else None
+
+
 def gemm_reference(dev, n=16384, iters=10):
     """Sustained rate of a plain bf16 GEMM (n x n x n through torch.matmul, i.e. the vendor BLAS)
     on this part in the same run: a reference for how much of the spec-sheet matrix-core peak the
@@ -373,6 +409,52 @@ def bench_decode(w, iters, dev, copies=4):
     med = ms[len(ms) // 2]
     return dict(median_ms=med, min_ms=ms[0], b2b_ms=b2b, bytes=alg, gbs=alg / (med * 1e-3) / 1e9,
                 b2b_gbs=alg / (b2b * 1e-3) / 1e9)
+
+
+def bench_decode_sharded(w, iters, dev, shards=4, copies=6):
+    """The decode batch with its cache split along the length into ``shards`` equal slices, one
+    per rank of an inference context-parallel job: each rank decodes over its own slice (the
+    one-GPU part, timed slice by slice, rotating ``copies`` copies of the slice so reads come
+    from HBM), then the ranks' (o, LSE) partials, once all-gathered, are combined by
+    gqa_decode_merge (timed on its own). The all-gather itself needs a second GPU."""
+    import context_causal_attention_load_amd as cpa
+    from context_causal_attention_load_amd import synth
+
+    lengths, q, kc, vc = synth.workload_decode_inputs(w)
+    W = w.max_len // shards
+    qd = q.to(dev)
+    o_parts = torch.empty((shards, w.batch, w.hq, w.d), dtype=w.dtype, device=dev)
+    l_parts = torch.empty((shards, w.batch, w.hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(cpa.decode_workspace_bytes(w.batch, w.hq, w.hkv, W, w.d), dtype=torch.uint8, device=dev)
+    per = []
+    for r in range(shards):
+        n = torch.clamp(lengths - r * W, 0, W).to(torch.int32)
+        nd = n.to(dev)
+        sl = [(kc[:, :, r * W:(r + 1) * W].contiguous().to(dev), vc[:, :, r * W:(r + 1) * W].contiguous().to(dev))]
+        for _ in range(copies - 1):
+            sl.append((sl[0][0].clone(), sl[0][1].clone()))
+
+        def call(i, sl=sl, nd=nd, r=r):
+            kci, vci = sl[i % copies]
+            cpa.decode(qd, kci, vci, nd, scale=w.scale, workspace=ws, out=o_parts[r], lse=l_parts[r])
+
+        for i in range(copies):
+            call(i)
+        torch.cuda.synchronize()
+        ms, b2b = _time_calls(call, iters)
+        gms = _time_graph(call, lambda r=r: (o_parts[r], l_parts[r]), reps=4 * copies)
+        alg = decode_bytes(w, n)
+        per.append(dict(median_ms=ms[len(ms) // 2], b2b_ms=b2b, graph_ms=gms, bytes=alg, keys=int(n.sum())))
+        del sl, call
+    out = torch.empty((w.batch, w.hq, w.d), dtype=w.dtype, device=dev)
+    lse = torch.empty((w.batch, w.hq), dtype=torch.float32, device=dev)
+    cpa.decode_merge(o_parts, l_parts, out=out, lse=lse)
+    torch.cuda.synchronize()
+    mms, mb2b = _time_calls(lambda i: cpa.decode_merge(o_parts, l_parts, out=out, lse=lse), iters)
+    mgms = _time_graph(lambda i: cpa.decode_merge(o_parts, l_parts, out=out, lse=lse), lambda: (out, lse))
+    return dict(shards=per, merge_median_ms=mms[len(mms) // 2], merge_b2b_ms=mb2b, merge_graph_ms=mgms,
+                merge_bytes=o_parts.numel() * o_parts.element_size() + l_parts.numel() * 4
+                + out.numel() * out.element_size() + lse.numel() * 4)
 
 
 def bench_decode_int8(w, iters, dev, copies=6):
@@ -594,6 +676,30 @@ def main():
                          "traffic": profiled_traffic("decode_int8_mixtral8x22b_b24_l2048.md",
                                                      ("decode_int8.hip", "decode.hip", "common.h")),
                          "traffic_unit": "HBM bytes per call (split + merge)", "algorithmic_bytes": d8["bytes"]}}
+        ds = bench_decode_sharded(dw, args.decode_iters, dev)
+        busiest = max(ds["shards"], key=lambda s: s["median_ms"])
+        bgbs = busiest["bytes"] / (busiest["median_ms"] * 1e-3) / 1e9
+        us = lambda x: None if x is None else round(x * 1e3, 2)
+        result["decode_length_sharded"] = {
+            "workload": dw.name + f" with the cache split along its length into {len(ds['shards'])} slices "
+                        "(one per rank of an inference context-parallel job)",
+            "value": round(bgbs, 1), "unit": "GB/s (the slowest rank's slice)",
+            "shard_median_us": [round(s["median_ms"] * 1e3, 2) for s in ds["shards"]],
+            "shard_back_to_back_us": [round(s["b2b_ms"] * 1e3, 2) for s in ds["shards"]],
+            "shard_graph_replay_us": [us(s["graph_ms"]) for s in ds["shards"]],
+            "shard_keys": [s["keys"] for s in ds["shards"]],
+            "merge_median_us": round(ds["merge_median_ms"] * 1e3, 2),
+            "merge_back_to_back_us": round(ds["merge_b2b_ms"] * 1e3, 2),
+            "merge_graph_replay_us": us(ds["merge_graph_ms"]),
+            "timing_note": "median and back-to-back figures are host-issued calls (each includes the "
+                           "binding's checks and a launch); graph-replay figures are GPU time per call",
+            "rank_critical_path_us": round((busiest["median_ms"] + ds["merge_median_ms"]) * 1e3, 2),
+            "rank_critical_path_graph_replay_us": (
+                None if ds["merge_graph_ms"] is None or any(s["graph_ms"] is None for s in ds["shards"])
+                else us(max(s["graph_ms"] for s in ds["shards"]) + ds["merge_graph_ms"])),
+            "roofline": {"bound": "hbm", "achieved": round(bgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(bgbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "algorithmic_bytes": busiest["bytes"]}}
     if not args.no_other_configs:
         result["other_configs"] = other_configs_ms(dev)
     if not args.no_gemm_reference:

@@ -334,7 +334,7 @@ int cp_attention_bwd(const void* q_shard, const void* k, const void* v, const vo
 
 size_t gqa_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t max_len, int32_t d) {
   if (batch <= 0 || hq <= 0 || hkv <= 0 || max_len <= 0 || d <= 0) return 0;
-  return (size_t)batch * hq * decode_nsplit(max_len) * (size_t)(d + 2) * sizeof(float);
+  return (size_t)batch * hq * decode_ws_nsplit(max_len) * (size_t)(d + 2) * sizeof(float);
 }
 
 }  // extern "C"
@@ -370,7 +370,7 @@ int decode_checked(const char* where, const void* q, const void* k_cache, const 
       return fail(CPA_EINVAL,
                   "%s: this call needs %zu bytes of split partials (batch %d x hq %d x %d splits x (d + 2) floats), "
                   "more than the library's static scratch of %zu bytes; use gqa_decode_attention with a workspace",
-                  where, need, batch, hq, decode_nsplit(max_len), (size_t)kDecodeNoAllocScratchBytes);
+                  where, need, batch, hq, decode_ws_nsplit(max_len), (size_t)kDecodeNoAllocScratchBytes);
   } else if (workspace_bytes < need) {
     return fail(CPA_EINVAL, "%s: workspace of %zu bytes, need %zu", where, workspace_bytes, need);
   }

@@ -166,6 +166,16 @@ hipError_t launch_decode_split_merge(const int32_t* lengths, float* ws, void* o,
 // the split's max and sum (log2 units).
 constexpr int kDecodeSplitLen = 256;
 inline int decode_nsplit(int max_len) { return (max_len + kDecodeSplitLen - 1) / kDecodeSplitLen; }
+// A short cache (a length slice of an inference context-parallel job, say) has too few 256-key
+// splits to fill the part, so the v_dot2 decode kernels take 128-key splits up to this length.
+constexpr int kDecodeShortSplitLen = 128;
+constexpr int kDecodeShortMaxLen = 1024;
+inline bool decode_short_cache(int max_len) { return max_len <= kDecodeShortMaxLen; }
+// Split partials a decode workspace must hold per (sequence, query head): the most any path takes.
+inline int decode_ws_nsplit(int max_len) {
+  return decode_short_cache(max_len) ? (max_len + kDecodeShortSplitLen - 1) / kDecodeShortSplitLen
+                                     : decode_nsplit(max_len);
+}
 
 // Size of the file-scope device array that replaces the caller workspace in the
 // allocation-free decode call (one copy per GPU, held until the process ends).

@@ -340,8 +340,64 @@ __global__ __launch_bounds__(256) void decode_lse_merge_kernel(const T* __restri
   if (lse_out && threadIdx.x == 0) lse_out[bh] = empty ? -INFINITY : M + __builtin_amdgcn_logf(L) * kLn2;
 }
 
+// The same merge for up to 8 parts and D <= 256 with one thread per dim: every part's
+// log-sum-exp and output element are loaded before any arithmetic, so the block waits on one
+// round of loads instead of one per dependent step. An empty part's output (whatever it holds)
+// is dropped by a select, not multiplied by its zero weight.
+template <typename T, int R>
+__global__ __launch_bounds__(256) void decode_lse_merge_r_kernel(const T* __restrict__ o_parts,
+                                                                 const float* __restrict__ lse_parts, T* __restrict__ out,
+                                                                 float* __restrict__ lse_out, int64_t BH, int D) {
+  const int64_t bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const int dd = d < D ? d : D - 1;  // threads past the last dim load it again and store nothing
+  float lr[R], ov[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    lr[r] = lse_parts[r * BH + bh];
+    ov[r] = to_float(o_parts[(r * BH + bh) * D + dd]);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < R; ++r) M = fmaxf(M, lr[r]);
+  const bool empty = M == -INFINITY;
+  float L = 0.f, acc = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool live = lr[r] != -INFINITY;
+    const float wr = __builtin_amdgcn_exp2f((lr[r] - M) * kLog2e);
+    L += live ? wr : 0.f;
+    acc += live ? wr * ov[r] : 0.f;
+  }
+  if (d < D) out[bh * D + d] = empty ? (T)0.f : (T)(acc / L);
+  if (lse_out && d == 0) lse_out[bh] = empty ? -INFINITY : M + __builtin_amdgcn_logf(L) * kLn2;
+}
+
+template <typename T>
+void launch_lse_merge(const DecodeMergeArgs& a, int64_t bh, hipStream_t stream) {
+  const T* op = static_cast<const T*>(a.o_parts);
+  T* o = static_cast<T*>(a.o);
+  const int threads = a.d >= 256 ? 256 : ((a.d + 63) / 64) * 64;
+  if (a.d <= 256 && a.parts >= 1 && a.parts <= 8) {
+    switch (a.parts) {
+#define CPA_MERGE_R(R)                                                                                          \
+  case R:                                                                                                      \
+    hipLaunchKernelGGL((decode_lse_merge_r_kernel<T, R>), dim3((unsigned)bh), dim3(threads), 0, stream, op,   \
+                       a.lse_parts, o, a.lse, bh, a.d);                                                        \
+    return;
+      CPA_MERGE_R(1) CPA_MERGE_R(2) CPA_MERGE_R(3) CPA_MERGE_R(4) CPA_MERGE_R(5) CPA_MERGE_R(6) CPA_MERGE_R(7)
+      CPA_MERGE_R(8)
+#undef CPA_MERGE_R
+    }
+  }
+  hipLaunchKernelGGL(decode_lse_merge_kernel<T>, dim3((unsigned)bh), dim3(threads), 0, stream, op, a.lse_parts, o,
+                     a.lse, a.parts, bh, a.d);
+}
+
 // ------------------------------------------------------------------------------------------
-// bf16 fast path: one workgroup of 512 threads per (split of 256 keys, kv head, sequence)
+// bf16 fast path: one workgroup of 512 threads per (split of 256 keys, kv head, sequence); a
+// cache of at most 1024 keys takes 128-key splits instead, so that it still spreads over the
+// part (the merge reads the split length from the parameters)
 // ------------------------------------------------------------------------------------------
 constexpr int kFastThreads = 512;
 constexpr int kFastWaves = kFastThreads / 64;
@@ -366,9 +422,8 @@ __device__ __forceinline__ float dpp_quad_xor1(float x) {
 __device__ __forceinline__ float dpp_quad_xor2(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
 }
-template <int D, int G>
+template <int D, int G, int SL>
 __global__ __launch_bounds__(kFastThreads, 6) void decode_bf16_split_kernel(DecParams p) {
-  constexpr int SL = kDecodeSplitLen;
   constexpr int KC = D / 32;              // 16-byte K chunks per lane (4 lanes per key row)
   constexpr int KROWS = kFastThreads / 4;  // key rows per K pass
   constexpr int KP = SL / KROWS;           // K passes
@@ -756,8 +811,12 @@ void launch_mfma_128(const DecParams& p, hipStream_t stream) {
 
 template <int D, int G>
 void launch_fast(const DecParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_bf16_split_kernel<D, G>), dim3(decode_xcd_blocks(p.nsplit, p.Hkv, p.B)),
-                     dim3(kFastThreads), 0, stream, p);
+  if (p.split_len == kDecodeShortSplitLen)
+    hipLaunchKernelGGL((decode_bf16_split_kernel<D, G, kDecodeShortSplitLen>),
+                       dim3(decode_xcd_blocks(p.nsplit, p.Hkv, p.B)), dim3(kFastThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_bf16_split_kernel<D, G, kDecodeSplitLen>), dim3(decode_xcd_blocks(p.nsplit, p.Hkv, p.B)),
+                       dim3(kFastThreads), 0, stream, p);
 }
 
 bool launch_fast_128(const DecParams& p, hipStream_t stream) {
@@ -808,8 +867,14 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   p.scale_log2 = a.scale * kLog2e;
   if (p.B == 0 || p.Hq == 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    if (a.d == 128 && launch_fast_128(p, stream)) {
-      launch_merge<T, 128>(p, stream);
+    // the v_dot2 kernels: 128-key splits for a short cache, else the default 256
+    DecParams pf = p;
+    if (decode_short_cache(p.max_len)) {
+      pf.split_len = kDecodeShortSplitLen;
+      pf.nsplit = (p.max_len + kDecodeShortSplitLen - 1) / kDecodeShortSplitLen;
+    }
+    if (a.d == 128 && launch_fast_128(pf, stream)) {
+      launch_merge<T, 128>(pf, stream);
       return hipGetLastError();
     }
     if (a.d == 128) {  // G > 8
@@ -817,8 +882,8 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
       launch_merge<T, 128>(p, stream);
       return hipGetLastError();
     }
-    if (a.d == 64 && launch_fast_64(p, stream)) {
-      launch_merge<T, 64>(p, stream);
+    if (a.d == 64 && launch_fast_64(pf, stream)) {
+      launch_merge<T, 64>(pf, stream);
       return hipGetLastError();
     }
   }
@@ -905,16 +970,10 @@ hipError_t launch_decode_split_merge(const int32_t* lengths, float* ws, void* o,
 hipError_t launch_decode_merge(const DecodeMergeArgs& a, hipStream_t stream) {
   const int64_t bh = (int64_t)a.batch * a.hq;
   if (bh == 0) return hipSuccess;
-  const int threads = a.d >= 256 ? 256 : ((a.d + 63) / 64) * 64;
-  if (a.bf16) {
-    hipLaunchKernelGGL(decode_lse_merge_kernel<__bf16>, dim3((unsigned)bh), dim3(threads), 0, stream,
-                       static_cast<const __bf16*>(a.o_parts), a.lse_parts, static_cast<__bf16*>(a.o), a.lse, a.parts, bh,
-                       a.d);
-  } else {
-    hipLaunchKernelGGL(decode_lse_merge_kernel<float>, dim3((unsigned)bh), dim3(threads), 0, stream,
-                       static_cast<const float*>(a.o_parts), a.lse_parts, static_cast<float*>(a.o), a.lse, a.parts, bh,
-                       a.d);
-  }
+  if (a.bf16)
+    launch_lse_merge<__bf16>(a, bh, stream);
+  else
+    launch_lse_merge<float>(a, bh, stream);
   return hipGetLastError();
 }
 

@@ -221,6 +221,9 @@ int cp_attention_bwd(const void* q_shard, const void* k, const void* v, const vo
  *            Its contents on entry do not matter. Calls sharing one workspace must not overlap.
  * Supported: bf16 and f32 with D in {64, 128}. CPA_EINVAL for hq % hkv != 0, null or misaligned
  * pointers, a workspace that is too small, or a non-positive scale. */
+/* gqa_decode_workspace_bytes: batch x hq x nsplit x (d + 2) floats of split partials, with
+ * nsplit = ceil(max_len / 128) for max_len <= 1024 (short caches take 128-key splits, so that
+ * they still fill the part) and ceil(max_len / 256) beyond; 0 for a non-positive argument. */
 size_t gqa_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t hkv, int32_t max_len, int32_t d);
 
 int gqa_decode_attention(const void* q, const void* k_cache, const void* v_cache,

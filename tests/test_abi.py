@@ -395,6 +395,10 @@ def test_decode_workspace_size(lib):
     # (max, sum, D outputs) per (sequence, query head, split of 256 keys)
     assert cpa.decode_workspace_bytes(24, 48, 8, 2048, 128) == 24 * 48 * 8 * 130 * 4
     assert cpa.decode_workspace_bytes(1, 1, 1, 1, 64) == 66 * 4
+    # short caches (max_len <= 1024) take 128-key splits
+    assert cpa.decode_workspace_bytes(24, 48, 8, 512, 128) == 24 * 48 * 4 * 130 * 4
+    assert cpa.decode_workspace_bytes(2, 4, 1, 1024, 64) == 2 * 4 * 8 * 66 * 4
+    assert cpa.decode_workspace_bytes(2, 4, 1, 1025, 64) == 2 * 4 * 5 * 66 * 4
     assert cpa.decode_workspace_bytes(0, 48, 8, 2048, 128) == 0
 
 

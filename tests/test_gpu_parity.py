@@ -462,6 +462,41 @@ def test_decode_length_sharded_merge(shape):
     assert_close(L.cpu().numpy(), L_ref, tol, f"sharded decode LSE ({shape})")
 
 
+@pytest.mark.parametrize("R,B,Hq,D,dtype", [
+    (1, 3, 5, 128, torch.bfloat16),
+    (4, 24, 48, 128, torch.bfloat16),   # the length-sharded Mixtral decode's merge
+    (8, 2, 6, 64, torch.float32),
+    (5, 2, 3, 200, torch.bfloat16),     # D not a multiple of 64: threads past it store nothing
+    (9, 2, 4, 128, torch.float32),      # more parts than the unrolled kernel takes
+    (3, 2, 3, 300, torch.float32),      # D above 256
+])
+def test_decode_merge_against_oracle(R, B, Hq, D, dtype):
+    """gqa_decode_merge on random partials against the oracle's merge: some parts empty
+    (log-sum-exp -inf) with NaN in their outputs, which must not reach the result, and one
+    (b, h) with every part empty (O = 0, LSE = -inf)."""
+    announce(f"decode merge R={R} B={B} Hq={Hq} D={D} {dtype}")
+    g = torch.Generator().manual_seed(R * 1000 + D)
+    o = torch.randn((R, B, Hq, D), generator=g).to(dtype)
+    lse = (torch.rand((R, B, Hq), generator=g) * 10 - 5).float()
+    empty = torch.rand((R, B, Hq), generator=g) < 0.3
+    empty[:, 0, 0] = True  # every part of (0, 0) empty
+    if R > 1:
+        empty[0, 1, 0] = False
+        empty[1:, 1, 0] = True  # (1, 0): one live part
+    lse[empty] = -float("inf")
+    o[empty] = float("nan")
+    O, L = cpa.decode_merge(o.to(DEV), lse.to(DEV))
+    torch.cuda.synchronize()
+    O_ref, L_ref = oatt.decode_merge_ref(o, lse)
+    tol = TOL[dtype]
+    assert_close(O.float().cpu().numpy(), O_ref, tol, "merge O")
+    Lg = L.cpu().numpy()
+    assert np.isneginf(Lg[0, 0]) and np.isneginf(L_ref[0, 0])
+    fin = np.isfinite(L_ref)
+    assert np.array_equal(np.isfinite(Lg), fin)
+    assert_close(Lg[fin], L_ref[fin], tol, "merge LSE")
+
+
 def test_decode_workspace_reuse():
     """One workspace (garbage-filled) serves repeated calls and a smaller batch afterwards."""
     announce("decode workspace reuse")

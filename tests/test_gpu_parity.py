@@ -369,6 +369,11 @@ def test_decode_full_workload_with_poisoned_tail():
     (2, 8, 8, 64, 513, torch.float32, [513, 17]),
     (5, 12, 4, 64, 1000, torch.bfloat16, [999, 1000, 512, 3, 768]),
     (2, 4, 2, 128, 64, torch.float32, [64, 33]),
+    # caches up to 1024 keys take 128-key splits in the v_dot2 kernels, longer ones 256
+    (3, 12, 2, 128, 1024, torch.bfloat16, [1024, 128, 129]),
+    (3, 12, 2, 128, 1025, torch.bfloat16, [1025, 1024, 1]),
+    (2, 8, 2, 64, 128, torch.bfloat16, [128, 127]),
+    (2, 8, 2, 64, 129, torch.bfloat16, [129, 128]),
     # 12 kv heads: workgroups are placed by kv head on 8 XCDs, so heads 8..11 form a second group
     (2, 24, 12, 128, 700, torch.bfloat16, [700, 300]),
     (2, 36, 12, 64, 200, torch.float32, [200, 1]),

@@ -969,19 +969,20 @@ struct Dkv16Cfg {
 };
 
 // Chunk swizzle of the 16-key kernel's tiles (a 16-byte chunk c of row r sits at c ^ swz16(r)).
-// LDS serves 256 bytes a cycle: a 16-byte read is served 16 lanes at a time, an 8-byte read 32.
-// The S reads take one chunk of 16 consecutive rows, so swz16 is one-to-one on those (with a
-// 384-byte row at Dqk 192, separately on even and odd rows, which sit 128 bytes apart). A
-// transposing read takes a chunk pair {2 m, 2 m + 1} of rows 8 k .. 8 k + 7, so swz16 / 2 is
-// one-to-one on those rows (at Dqk 192 again separately on even and odd rows). The 32-key
-// kernel's swizzle spreads only rows 0..3 apart, which its transposing reads need.
+// The S reads take one chunk of 16 consecutive rows, a transposing read a chunk pair
+// {2 m, 2 m + 1} of rows 8 k .. 8 k + 7. The two forms were chosen by timing each read pattern
+// on the part with the LDS bank-conflict counter. The 16-chunk (dO) form keeps the transposing
+// reads conflict-free and leaves the S reads two-way conflicted; no form tried kept both free.
+// The 24-chunk (Q, Dqk 192) form, row & 7, keeps both conflict-free: its 384-byte rows already
+// spread rows apart by 128 bytes, and row & 7 spreads rows 8 apart. Both forms depend on row
+// bits 0..3 only and stay below 8 on 24-chunk rows (the offsets below rely on that).
 template <int CH>
 __device__ __forceinline__ int swz16(int row) {
   static_assert(CH % 16 == 0 || CH % 16 == 8, "tiles of 16 or 24 chunks per row");
   if constexpr (CH % 16 == 0) {
     return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
   } else {
-    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+    return row & 7;
   }
 }
 
